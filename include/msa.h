@@ -1,0 +1,234 @@
+/*
+ * msa.h — C ABI of the MSA (Memory Sparse Attention) inference hot path for
+ * AMD MI355X (gfx950).
+ *
+ * The method (the MSA pages, arXiv 2603.23516):
+ *   Stage 1, offline encoding: every document's K, V and router keys K^R are
+ *     mean-pooled over fixed 64-token chunks, K under document-wise RoPE
+ *     (positions restart at 0 in each document).
+ *   Stage 2, online routing: the router query Q^R is scored against every
+ *     pooled router key by cosine similarity (mean over heads, max over query
+ *     tokens), chunk scores are max-reduced to document scores and the top-16
+ *     documents are selected.
+ *   Stage 3, sparse generation: the query attends over the selected documents'
+ *     pooled K/V concatenated with its local KV, under global RoPE whose
+ *     positions start at k.
+ *   Memory Interleave repeats route → select → attend as new tokens arrive.
+ * Sources: portal.techblg.uk IRMaD reading, section M "Materials & Methods"
+ * (architecture, routing/sparse-attention, positional-encoding, three-stage
+ * inference, Memory Parallel and Memory Interleave bullets); paper.rainbus.top
+ * "method steps"; chooseai.io sections 2.1-2.4; zhichai.net "关键技术细节".
+ *
+ * Conventions for every call:
+ *   - Return value: MSA_OK (0) or a negative msa_status. On an error nothing
+ *     has been enqueued and no output has been written; msa_last_error()
+ *     returns a thread-local message.
+ *   - Success means the work is enqueued on `stream` (a hipStream_t passed as
+ *     void*; NULL is the legacy default stream). Results are valid after the
+ *     stream is synchronised.
+ *   - Pointers are device pointers unless the name ends in `_h` (host memory).
+ *     Where a call says so, K̄/V̄ may instead live in pinned host memory
+ *     (hipHostMalloc, or torch pin_memory=True); pageable host memory is
+ *     rejected.
+ *   - The caller owns every buffer, including workspaces (sized by the
+ *     *_workspace calls). The library keeps no allocation and no state across
+ *     calls except the thread-local error string.
+ *   - Inputs are never modified, except where a call says so.
+ *   - bf16 tensors are raw bit patterns (msa_bf16), row-major and contiguous:
+ *     token-major raw states [T, H, 128], pooled states [C, H, 128].
+ *   - Offsets are int64 CSR: document i owns tokens [dto[i], dto[i+1]) and
+ *     chunks [dco[i], dco[i+1]). Kernels clamp every index they derive from
+ *     device arrays, so malformed offsets give wrong values, never an
+ *     out-of-bounds access.
+ *   - Calls are re-entrant; two calls may run concurrently on different
+ *     streams if they share no output or workspace buffer.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t msa_bf16; /* bf16 storage (upper half of an IEEE binary32) */
+
+typedef enum msa_status {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = -1, /* null pointer, bad enum, unsupported memory kind */
+  MSA_ERR_SHAPE = -2,       /* sizes inconsistent or out of range */
+  MSA_ERR_WORKSPACE = -3,   /* workspace missing or too small */
+  MSA_ERR_HIP = -4,         /* a HIP runtime call or launch failed */
+  MSA_ERR_UNSUPPORTED = -5  /* valid but not implemented (e.g. head_dim != 128) */
+} msa_status;
+
+enum { MSA_TOKEN_REDUCE_MAX = 0, MSA_TOKEN_REDUCE_MEAN = 1 };
+enum { MSA_DOC_ROPE_TOKEN = 0, MSA_DOC_ROPE_CHUNK = 1 };
+
+/* Model dimensions. Defaults (msa_default_dims) follow the pages'
+ * architecture bullet (section M): 8 KV and router heads of dimension 128,
+ * chunk P = 64, top-k = 16; 32 query heads (GQA group 4); RoPE base 1e6.
+ * token_reduce: how chunk scores reduce over the query's tokens — MAX (the
+ *   explicit routing formula of section M) or MEAN (the method-steps wording
+ *   of paper.rainbus.top).
+ * doc_rope_mode: TOKEN rotates raw K at its document-local token position
+ *   before pooling; CHUNK rotates the pooled chunk at its chunk index.
+ * Supported: head_dim == 128, n_kv_heads == n_router_heads == 8,
+ *   n_q_heads a multiple of n_kv_heads (<= 64), chunk in [1, 64],
+ *   top_k in [1, 64]. */
+typedef struct msa_dims {
+  int32_t n_kv_heads;
+  int32_t n_router_heads;
+  int32_t n_q_heads;
+  int32_t head_dim;
+  int32_t chunk;
+  int32_t top_k;
+  float rope_theta;
+  int32_t token_reduce;
+  int32_t doc_rope_mode;
+} msa_dims;
+
+/* Fills *d with the defaults above. */
+void msa_default_dims(msa_dims* d);
+
+/* Thread-local message of the last failed call on this thread ("" if none). */
+const char* msa_last_error(void);
+
+/* ABI version of this header (bumped on any signature change). */
+int32_t msa_abi_version(void);
+#define MSA_ABI_VERSION 1
+
+/* ------------------------------------------------------------------------ */
+/* Chunk plan (host, pure). Each document is cut into ceil(n_i / chunk)
+ * chunks of `chunk` tokens, the last one possibly partial; a chunk never
+ * spans two documents (chooseai.io section 2.1; techblg lay summary ③).
+ *   doc_token_offsets_h [n_docs+1] (host): non-decreasing from 0, every
+ *     document at least one token (MSA_ERR_SHAPE otherwise).
+ *   doc_chunk_offsets_h [n_docs+1] (host, written).
+ * Returns MSA_OK and writes nothing on error. */
+int32_t msa_plan_chunks(const int64_t* doc_token_offsets_h, int32_t n_docs, int32_t chunk,
+                        int64_t* doc_chunk_offsets_h);
+
+/* ------------------------------------------------------------------------ */
+/* Stage 1: pooling with document-wise RoPE (techblg section M, routing and
+ * positional-encoding bullets: K̄ = φ(K), V̄ = φ(V), K̄^R = φ(K^R), φ the chunk
+ * mean; positions restart at 0 per document).
+ *   K, V   [n_tokens, n_kv_heads, 128] bf16; KR [n_tokens, n_router_heads, 128].
+ *   doc_token_offsets, doc_chunk_offsets: device int64 [n_docs+1]; the chunk
+ *     offsets must be the plan of the token offsets (msa_plan_chunks).
+ *   Kbar, Vbar [n_chunks, n_kv_heads, 128], KRbar [n_chunks, n_router_heads,
+ *     128] bf16 (written). Each output is the mean over the chunk's actual
+ *     tokens, accumulated in fp64 and rounded to bf16 nearest-even.
+ *   Any of Kbar/Vbar/KRbar may be NULL to skip that output.
+ *   ws / ws_bytes: workspace of at least msa_encode_pool_workspace() bytes. */
+size_t msa_encode_pool_workspace(const msa_dims* d, int32_t n_docs, int64_t n_chunks);
+int32_t msa_encode_pool(const msa_dims* d, const msa_bf16* K, const msa_bf16* V,
+                        const msa_bf16* KR, const int64_t* doc_token_offsets,
+                        const int64_t* doc_chunk_offsets, int32_t n_docs, int64_t n_tokens,
+                        int64_t n_chunks, msa_bf16* Kbar, msa_bf16* Vbar, msa_bf16* KRbar,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Stage 2: routing and top-k (techblg section M, routing bullet:
+ * S_ij = max_t mean_h cos(Q^R_{t,h}, K̄^R_{ij,h}), s_i = max_j S_ij,
+ * I = Top-k({s_i})).
+ *   QR [B, M, n_router_heads, 128] bf16: B independent queries of M tokens.
+ *   KRbar [n_chunks, n_router_heads, 128] bf16, resident in device memory.
+ *   doc_chunk_offsets: device int64 [n_docs+1].
+ *   doc_scores [B, n_docs] fp32: written with s_i; when accumulate != 0 it is
+ *     read first and max-merged (s_i = max(previous, new)) — the incremental
+ *     form of re-routing every token of a growing query under the MAX token
+ *     reduction (MEAN with accumulate is MSA_ERR_UNSUPPORTED).
+ *   topk_ids [B, top_k] int32, topk_scores [B, top_k] fp32: the n_sel =
+ *     min(top_k, n_docs) best documents by (score descending, id ascending),
+ *     in rank order; entries past n_sel are -1 / -inf.
+ *   n_sel [B] int32 (written).
+ *   Norms are clamped at 1e-6 before dividing; a NaN score ranks last.
+ *   ws / ws_bytes: at least msa_route_topk_workspace() bytes. */
+size_t msa_route_topk_workspace(const msa_dims* d, int32_t B, int32_t M, int64_t n_chunks,
+                                int32_t n_docs);
+int32_t msa_route_topk(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
+                       const msa_bf16* KRbar, const int64_t* doc_chunk_offsets, int32_t n_docs,
+                       int64_t n_chunks, float* doc_scores, int32_t accumulate, int32_t* topk_ids,
+                       float* topk_scores, int32_t* n_sel, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Stage 3: context assembly, global RoPE and sparse attention (techblg
+ * section M, routing bullet: K_ctx = [{K̄_i}_{i∈I}; K_q], V_ctx likewise,
+ * Output = Attention(Q_q, K_ctx, V_ctx); positional bullet: the active
+ * context uses global RoPE with positions offset from k).
+ *   Q [M, n_q_heads, 128] bf16: the M query tokens, which are the last M of
+ *     the M_loc local tokens (M <= M_loc).
+ *   K_loc, V_loc [M_loc, n_kv_heads, 128] bf16: local (active-context) KV.
+ *     K_loc is rotated here at position pos0 + v unless k_loc_rotated != 0.
+ *   Kbar, Vbar [n_chunks, n_kv_heads, 128] bf16: pooled memory; device
+ *     memory, or pinned host memory when kv_on_host != 0 (read in place over
+ *     PCIe by the kernel; pageable memory is MSA_ERR_INVALID_ARG).
+ *   doc_chunk_offsets: device int64 [n_docs+1].
+ *   sel_ids [top_k] int32 and n_sel [1] int32 (device; as written by
+ *     msa_route_topk for one query). Ids outside [0, n_docs) are skipped.
+ *   max_sel_chunks: an upper bound on the selected documents' total chunk
+ *     count (e.g. top_k × the longest document's chunks); selections beyond
+ *     it are truncated to it.
+ *   pos0: global position of local token 0; -1 means n_sel (the reading "k").
+ *   Query token u (local index M_loc-M+u) sees every selected memory chunk and
+ *   local tokens 0..M_loc-M+u; q head h reads KV head h / (n_q_heads /
+ *   n_kv_heads); logits are scaled by 1/sqrt(128); softmax in fp32.
+ *   out [M, n_q_heads, 128] bf16 (written); out_f32 (may be NULL) receives the
+ *   same values in fp32.
+ *   ws / ws_bytes: at least msa_sparse_attend_workspace() bytes. */
+size_t msa_sparse_attend_workspace(const msa_dims* d, int32_t M, int32_t M_loc,
+                                   int64_t max_sel_chunks);
+int32_t msa_sparse_attend(const msa_dims* d, const msa_bf16* Q, int32_t M, const msa_bf16* K_loc,
+                          const msa_bf16* V_loc, int32_t M_loc, int32_t k_loc_rotated,
+                          const msa_bf16* Kbar, const msa_bf16* Vbar, int32_t kv_on_host,
+                          int64_t n_chunks, const int64_t* doc_chunk_offsets, int32_t n_docs,
+                          const int32_t* sel_ids, const int32_t* n_sel, int64_t max_sel_chunks,
+                          int64_t pos0, msa_bf16* out, float* out_f32, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Memory Interleave (techblg section M, Memory Interleave bullet; chooseai.io
+ * section 2.4): one round appends M_new tokens to the active context, routes
+ * them (max-merged into the running document scores), re-selects the top-k
+ * documents and attends the new tokens over [selected memory; every local
+ * token]. The state's buffers belong to the caller.
+ *   doc_scores [n_docs] fp32: running scores; set every entry to -inf (or call
+ *     msa_interleave_reset) before the first round.
+ *   K_loc, V_loc [cap_loc, n_kv_heads, 128] bf16: the raw (unrotated) local
+ *     keys/values; the round appends K_new/V_new at row n_loc.
+ *   n_loc: tokens already in K_loc/V_loc (host value, advanced by M_new on
+ *     success). cap_loc: capacity in tokens (MSA_ERR_SHAPE if exceeded).
+ *   topk_ids [top_k] int32, topk_scores [top_k] fp32, n_sel [1] int32: this
+ *     round's selection (written).
+ *   pos0: as in msa_sparse_attend (-1 means n_sel). */
+typedef struct msa_interleave_state {
+  float* doc_scores;
+  msa_bf16* K_loc;
+  msa_bf16* V_loc;
+  int32_t cap_loc;
+  int32_t n_loc;
+  int32_t* topk_ids;
+  float* topk_scores;
+  int32_t* n_sel;
+  int64_t pos0;
+} msa_interleave_state;
+
+int32_t msa_interleave_reset(msa_interleave_state* st, int32_t n_docs, void* stream);
+size_t msa_interleave_step_workspace(const msa_dims* d, int32_t M_new, int32_t cap_loc,
+                                     int64_t n_chunks, int32_t n_docs, int64_t max_sel_chunks);
+int32_t msa_interleave_step(const msa_dims* d, msa_interleave_state* st, const msa_bf16* Q_new,
+                            const msa_bf16* K_new, const msa_bf16* V_new, const msa_bf16* QR_new,
+                            int32_t M_new, const msa_bf16* KRbar, const msa_bf16* Kbar,
+                            const msa_bf16* Vbar, int32_t kv_on_host, int64_t n_chunks,
+                            const int64_t* doc_chunk_offsets, int32_t n_docs,
+                            int64_t max_sel_chunks, msa_bf16* out, void* ws, size_t ws_bytes,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H */

@@ -1,0 +1,13 @@
+"""MI355X-native hot path of Memory Sparse Attention (MSA).
+
+The compute lives in ``libmsa.so`` (hand-written HIP for gfx950, C ABI in
+``include/msa.h``); this package is its ctypes binding. Stages:
+``encode_pool`` (chunk mean-pooling with document RoPE), ``route_topk``
+(cosine routing, document max, top-k), ``sparse_attend`` (assembly, global
+RoPE, GQA attention) and ``Interleave`` (Memory Interleave rounds).
+"""
+from ._lib import (  # noqa: F401
+    DOC_ROPE_CHUNK, DOC_ROPE_TOKEN, EXPORTED, LIB_PATH, TOKEN_REDUCE_MAX, TOKEN_REDUCE_MEAN,
+    Dims, Interleave, MsaError, dims, encode_pool, lib, plan_chunks, route_topk,
+    route_topk_workspace, sparse_attend, sparse_attend_workspace,
+)

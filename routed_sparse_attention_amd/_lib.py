@@ -1,0 +1,285 @@
+"""ctypes binding of libmsa.so (C ABI declared in include/msa.h).
+
+Argument marshalling only: every step of the MSA path runs in the HIP
+library. PyTorch supplies device memory, pinned host memory, workspaces and
+the current stream. If the library is not built the calls raise; there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+MSA_OK = 0
+STATUS = {0: "MSA_OK", -1: "MSA_ERR_INVALID_ARG", -2: "MSA_ERR_SHAPE", -3: "MSA_ERR_WORKSPACE",
+          -4: "MSA_ERR_HIP", -5: "MSA_ERR_UNSUPPORTED"}
+TOKEN_REDUCE_MAX, TOKEN_REDUCE_MEAN = 0, 1
+DOC_ROPE_TOKEN, DOC_ROPE_CHUNK = 0, 1
+
+# every symbol include/msa.h declares
+EXPORTED = [
+    "msa_default_dims", "msa_last_error", "msa_abi_version", "msa_plan_chunks",
+    "msa_encode_pool_workspace", "msa_encode_pool", "msa_route_topk_workspace", "msa_route_topk",
+    "msa_sparse_attend_workspace", "msa_sparse_attend", "msa_interleave_reset",
+    "msa_interleave_step_workspace", "msa_interleave_step",
+]
+
+
+class MsaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("n_kv_heads", ctypes.c_int32), ("n_router_heads", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("token_reduce", ctypes.c_int32),
+                ("doc_rope_mode", ctypes.c_int32)]
+
+
+class InterleaveStateC(ctypes.Structure):
+    _fields_ = [("doc_scores", ctypes.c_void_p), ("K_loc", ctypes.c_void_p),
+                ("V_loc", ctypes.c_void_p), ("cap_loc", ctypes.c_int32),
+                ("n_loc", ctypes.c_int32), ("topk_ids", ctypes.c_void_p),
+                ("topk_scores", ctypes.c_void_p), ("n_sel", ctypes.c_void_p),
+                ("pos0", ctypes.c_int64)]
+
+
+_lib = None
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_DP = ctypes.POINTER(Dims)
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libmsa.so (raises ImportError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(hipcc, gfx950); the MSA path has no other implementation")
+    L = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "msa_default_dims": (None, [_DP]),
+        "msa_last_error": (ctypes.c_char_p, []),
+        "msa_abi_version": (_i32, []),
+        "msa_plan_chunks": (_i32, [_vp, _i32, _i32, _vp]),
+        "msa_encode_pool_workspace": (_sz, [_DP, _i32, _i64]),
+        "msa_encode_pool": (_i32, [_DP, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp,
+                                   _vp, _sz, _vp]),
+        "msa_route_topk_workspace": (_sz, [_DP, _i32, _i32, _i64, _i32]),
+        "msa_route_topk": (_i32, [_DP, _vp, _i32, _i32, _vp, _vp, _i32, _i64, _vp, _i32, _vp, _vp,
+                                  _vp, _vp, _sz, _vp]),
+        "msa_sparse_attend_workspace": (_sz, [_DP, _i32, _i32, _i64]),
+        "msa_sparse_attend": (_i32, [_DP, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i64,
+                                     _vp, _i32, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
+        "msa_interleave_reset": (_i32, [ctypes.POINTER(InterleaveStateC), _i32, _vp]),
+        "msa_interleave_step_workspace": (_sz, [_DP, _i32, _i32, _i64, _i32, _i64]),
+        "msa_interleave_step": (_i32, [_DP, ctypes.POINTER(InterleaveStateC), _vp, _vp, _vp, _vp,
+                                       _i32, _vp, _vp, _vp, _i32, _i64, _vp, _i32, _i64, _vp, _vp,
+                                       _sz, _vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != MSA_OK:
+        raise MsaError(rc, lib().msa_last_error().decode(errors="replace"))
+
+
+def dims(**kw) -> Dims:
+    d = Dims()
+    lib().msa_default_dims(ctypes.byref(d))
+    for k, v in kw.items():
+        if not hasattr(d, k):
+            raise TypeError(f"unknown dims field {k}")
+        setattr(d, k, v)
+    return d
+
+
+def _p(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, device_kind: str | None = "cuda", ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device_kind is not None and t.device.type != device_kind:
+        raise ValueError(f"{name} must be on {device_kind}, got {t.device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got shape {tuple(t.shape)}")
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+def plan_chunks(doc_token_offsets, chunk: int = 64) -> np.ndarray:
+    dto = np.ascontiguousarray(np.asarray(doc_token_offsets, dtype=np.int64))
+    out = np.zeros_like(dto)
+    _check(lib().msa_plan_chunks(dto.ctypes.data, len(dto) - 1, chunk, out.ctypes.data))
+    return out
+
+
+def encode_pool(K, V, KR, doc_token_offsets, doc_chunk_offsets, n_chunks: int, d: Dims | None = None,
+                outputs=("K", "V", "KR"), out=None):
+    """Stage-1 pooling: returns (Kbar, Vbar, KRbar) bf16 [n_chunks, 8, 128]
+    (None for outputs not requested)."""
+    d = d or dims()
+    for t, n in ((K, "K"), (V, "V"), (KR, "KR")):
+        _need(t, n, torch.bfloat16, ndim=3)
+    _need(doc_token_offsets, "doc_token_offsets", torch.int64)
+    _need(doc_chunk_offsets, "doc_chunk_offsets", torch.int64)
+    n_docs = doc_token_offsets.numel() - 1
+    if out is None:
+        mk = lambda: torch.empty((n_chunks, K.shape[1], K.shape[2]), dtype=torch.bfloat16, device=K.device)
+        out = tuple(mk() if name in outputs else None for name in ("K", "V", "KR"))
+    Kb, Vb, Rb = out
+    ws = lib().msa_encode_pool_workspace(ctypes.byref(d), n_docs, n_chunks)
+    w = _workspace(ws, K.device)
+    _check(lib().msa_encode_pool(ctypes.byref(d), _p(K), _p(V), _p(KR), _p(doc_token_offsets),
+                                 _p(doc_chunk_offsets), n_docs, K.shape[0], n_chunks, _p(Kb), _p(Vb),
+                                 _p(Rb), _p(w), ws, _stream()))
+    return Kb, Vb, Rb
+
+
+def route_topk_workspace(B: int, M: int, n_chunks: int, n_docs: int, d: Dims | None = None) -> int:
+    d = d or dims()
+    return lib().msa_route_topk_workspace(ctypes.byref(d), B, M, n_chunks, n_docs)
+
+
+def route_topk(QR, KRbar, doc_chunk_offsets, d: Dims | None = None, doc_scores=None,
+               accumulate: bool = False, ws=None, outs=None):
+    """Stage-2 routing for B queries: returns (doc_scores [B,N] f32,
+    topk_ids [B,k] i32, topk_scores [B,k] f32, n_sel [B] i32)."""
+    d = d or dims()
+    _need(QR, "QR", torch.bfloat16, ndim=4)
+    _need(KRbar, "KRbar", torch.bfloat16, ndim=3)
+    _need(doc_chunk_offsets, "doc_chunk_offsets", torch.int64)
+    B, M = QR.shape[0], QR.shape[1]
+    n_docs = doc_chunk_offsets.numel() - 1
+    C = KRbar.shape[0]
+    dev = QR.device
+    if doc_scores is None:
+        if accumulate:
+            raise ValueError("accumulate needs doc_scores")
+        doc_scores = torch.empty((B, n_docs), dtype=torch.float32, device=dev)
+    if outs is None:
+        outs = (torch.empty((B, d.top_k), dtype=torch.int32, device=dev),
+                torch.empty((B, d.top_k), dtype=torch.float32, device=dev),
+                torch.empty((B,), dtype=torch.int32, device=dev))
+    ids, sc, ns = outs
+    need = lib().msa_route_topk_workspace(ctypes.byref(d), B, M, C, n_docs)
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, dev)
+    _check(lib().msa_route_topk(ctypes.byref(d), _p(QR), B, M, _p(KRbar), _p(doc_chunk_offsets),
+                                n_docs, C, _p(doc_scores), int(bool(accumulate)), _p(ids), _p(sc),
+                                _p(ns), _p(ws), ws.numel(), _stream()))
+    return doc_scores, ids, sc, ns
+
+
+def sparse_attend_workspace(M: int, M_loc: int, max_sel_chunks: int, d: Dims | None = None) -> int:
+    d = d or dims()
+    return lib().msa_sparse_attend_workspace(ctypes.byref(d), M, M_loc, max_sel_chunks)
+
+
+def sparse_attend(Q, K_loc, V_loc, Kbar, Vbar, doc_chunk_offsets, sel_ids, n_sel,
+                  max_sel_chunks: int, pos0: int = -1, k_loc_rotated: bool = False,
+                  d: Dims | None = None, want_f32: bool = False, ws=None, out=None):
+    """Stage-3 sparse attention for one query: returns out bf16 [M, Hq, 128]
+    (and fp32 when want_f32). Kbar/Vbar may be pinned host tensors."""
+    d = d or dims()
+    _need(Q, "Q", torch.bfloat16, ndim=3)
+    _need(K_loc, "K_loc", torch.bfloat16, ndim=3)
+    _need(V_loc, "V_loc", torch.bfloat16, ndim=3)
+    on_host = Kbar.device.type == "cpu"
+    for t, n in ((Kbar, "Kbar"), (Vbar, "Vbar")):
+        _need(t, n, torch.bfloat16, device_kind=None, ndim=3)
+        if (t.device.type == "cpu") != on_host:
+            raise ValueError("Kbar and Vbar must both be on the GPU or both in pinned host memory")
+        if on_host and not t.is_pinned():
+            raise ValueError(f"{n}: host memory must be pinned")
+    _need(doc_chunk_offsets, "doc_chunk_offsets", torch.int64)
+    _need(sel_ids, "sel_ids", torch.int32)
+    _need(n_sel, "n_sel", torch.int32)
+    M, M_loc = Q.shape[0], K_loc.shape[0]
+    dev = Q.device
+    if out is None:
+        out = torch.empty(Q.shape, dtype=torch.bfloat16, device=dev)
+    of = torch.empty(Q.shape, dtype=torch.float32, device=dev) if want_f32 else None
+    need = lib().msa_sparse_attend_workspace(ctypes.byref(d), M, M_loc, max_sel_chunks)
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, dev)
+    _check(lib().msa_sparse_attend(ctypes.byref(d), _p(Q), M, _p(K_loc), _p(V_loc), M_loc,
+                                   int(bool(k_loc_rotated)), _p(Kbar), _p(Vbar), int(on_host),
+                                   Kbar.shape[0], _p(doc_chunk_offsets),
+                                   doc_chunk_offsets.numel() - 1, _p(sel_ids), _p(n_sel),
+                                   max_sel_chunks, pos0, _p(out), _p(of), _p(ws), ws.numel(),
+                                   _stream()))
+    return (out, of) if want_f32 else out
+
+
+class Interleave:
+    """Memory Interleave state for one query (caller-owned device buffers)."""
+
+    def __init__(self, n_docs: int, cap_loc: int, device="cuda", d: Dims | None = None,
+                 pos0: int = -1):
+        self.d = d or dims()
+        self.n_docs = n_docs
+        self.doc_scores = torch.empty((n_docs,), dtype=torch.float32, device=device)
+        self.K_loc = torch.zeros((cap_loc, 8, 128), dtype=torch.bfloat16, device=device)
+        self.V_loc = torch.zeros((cap_loc, 8, 128), dtype=torch.bfloat16, device=device)
+        self.topk_ids = torch.empty((self.d.top_k,), dtype=torch.int32, device=device)
+        self.topk_scores = torch.empty((self.d.top_k,), dtype=torch.float32, device=device)
+        self.n_sel = torch.empty((1,), dtype=torch.int32, device=device)
+        self.st = InterleaveStateC(_p(self.doc_scores), _p(self.K_loc), _p(self.V_loc), cap_loc, 0,
+                                   _p(self.topk_ids), _p(self.topk_scores), _p(self.n_sel), pos0)
+        _check(lib().msa_interleave_reset(ctypes.byref(self.st), n_docs, _stream()))
+
+    @property
+    def n_loc(self) -> int:
+        return self.st.n_loc
+
+    def step(self, Q_new, K_new, V_new, QR_new, KRbar, Kbar, Vbar, doc_chunk_offsets,
+             max_sel_chunks: int, ws=None, out=None):
+        d = self.d
+        for t, n in ((Q_new, "Q_new"), (K_new, "K_new"), (V_new, "V_new"), (QR_new, "QR_new")):
+            _need(t, n, torch.bfloat16, ndim=3)
+        _need(KRbar, "KRbar", torch.bfloat16, ndim=3)
+        on_host = Kbar.device.type == "cpu"
+        M_new = Q_new.shape[0]
+        dev = Q_new.device
+        if out is None:
+            out = torch.empty(Q_new.shape, dtype=torch.bfloat16, device=dev)
+        need = lib().msa_interleave_step_workspace(ctypes.byref(d), M_new, self.st.cap_loc,
+                                                   KRbar.shape[0], self.n_docs, max_sel_chunks)
+        if ws is None or ws.numel() < need:
+            ws = _workspace(need, dev)
+        _check(lib().msa_interleave_step(ctypes.byref(d), ctypes.byref(self.st), _p(Q_new),
+                                         _p(K_new), _p(V_new), _p(QR_new), M_new, _p(KRbar),
+                                         _p(Kbar), _p(Vbar), int(on_host), KRbar.shape[0],
+                                         _p(doc_chunk_offsets), self.n_docs, max_sel_chunks,
+                                         _p(out), _p(ws), ws.numel(), _stream()))
+        return out

@@ -1,0 +1,377 @@
+// C entry points of the MSA library: argument validation, workspace layout,
+// kernel selection and error reporting. Every check runs before anything is
+// enqueued, so a failed call leaves outputs untouched.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "msa_internal.h"
+
+namespace msa {
+
+static thread_local char g_err[1024] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+namespace {
+
+int check_dims(const msa_dims* d) {
+  if (d == nullptr) return fail(MSA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->head_dim != kDim)
+    return fail(MSA_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", d->head_dim);
+  if (d->n_kv_heads != kHeads || d->n_router_heads != kHeads)
+    return fail(MSA_ERR_UNSUPPORTED, "n_kv_heads=%d n_router_heads=%d unsupported (only 8)",
+                d->n_kv_heads, d->n_router_heads);
+  if (d->n_q_heads < kHeads || d->n_q_heads > 64 || d->n_q_heads % kHeads != 0)
+    return fail(MSA_ERR_SHAPE, "n_q_heads=%d must be a multiple of 8 in [8, 64]", d->n_q_heads);
+  if (d->chunk < 1 || d->chunk > 4096)
+    return fail(MSA_ERR_SHAPE, "chunk=%d out of [1, 4096]", d->chunk);
+  if (d->top_k < 1 || d->top_k > 64) return fail(MSA_ERR_SHAPE, "top_k=%d out of [1, 64]", d->top_k);
+  if (!(d->rope_theta > 1.0f) || !std::isfinite(d->rope_theta))
+    return fail(MSA_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  if (d->token_reduce != MSA_TOKEN_REDUCE_MAX && d->token_reduce != MSA_TOKEN_REDUCE_MEAN)
+    return fail(MSA_ERR_INVALID_ARG, "token_reduce=%d unknown", d->token_reduce);
+  if (d->doc_rope_mode != MSA_DOC_ROPE_TOKEN && d->doc_rope_mode != MSA_DOC_ROPE_CHUNK)
+    return fail(MSA_ERR_INVALID_ARG, "doc_rope_mode=%d unknown", d->doc_rope_mode);
+  return MSA_OK;
+}
+
+// Resolves a K̄/V̄ pointer: device memory as is, pinned host memory to its
+// device-visible address; pageable host memory is rejected.
+int resolve_kv(const void* p, int on_host, const void** out, const char* name) {
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MSA_ERR_INVALID_ARG, "%s: not a HIP allocation (%s)", name, hipGetErrorString(e));
+  }
+  if (on_host) {
+    if (attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr)
+      return fail(MSA_ERR_INVALID_ARG, "%s: kv_on_host needs pinned host memory", name);
+    // devicePointer is the mapping of the allocation's base; keep the offset.
+    const char* host_base = static_cast<const char*>(attr.hostPointer);
+    const char* dev_base = static_cast<const char*>(attr.devicePointer);
+    if (host_base != nullptr)
+      *out = dev_base + (static_cast<const char*>(p) - host_base);
+    else
+      *out = p;
+  } else {
+    if (attr.type != hipMemoryTypeDevice)
+      return fail(MSA_ERR_INVALID_ARG, "%s: expected device memory (pass kv_on_host=1 for "
+                  "pinned host memory)", name);
+    *out = p;
+  }
+  return MSA_OK;
+}
+
+// Routing plan: kernel choice and workspace offsets.
+struct RoutePlan {
+  bool mfma;
+  RouteGeom g;
+  int32_t n_slices;
+  size_t off_qh, off_ql, off_S, off_cand, total;
+};
+
+RoutePlan route_plan(int32_t B, int32_t M, int64_t C, int32_t N, int32_t K) {
+  RoutePlan p;
+  const int64_t rows = (int64_t)B * M;
+  p.mfma = false;
+  p.g = route_geom(B, M, kValuTileRows);
+  (void)rows;
+  p.n_slices = (N + kTopkSlice - 1) / kTopkSlice;
+  size_t o = 0;
+  const size_t qbytes = (size_t)B * M * kRowElems * 2;
+  p.off_qh = o; o = align_up(o + qbytes, 256);
+  p.off_ql = o; o = align_up(o + qbytes, 256);
+  p.off_S = o; o = align_up(o + (size_t)p.g.parts * B * C * 4, 256);
+  p.off_cand = o; o = align_up(o + (size_t)B * p.n_slices * K * 8, 256);
+  p.total = o;
+  return p;
+}
+
+int route_topk_impl(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
+                    const msa_bf16* KRbar, const int64_t* dco, int32_t n_docs, int64_t n_chunks,
+                    float* doc_scores, int32_t accumulate, int32_t* topk_ids, float* topk_scores,
+                    int32_t* n_sel, void* ws, size_t ws_bytes, hipStream_t s) {
+  const RoutePlan p = route_plan(B, M, n_chunks, n_docs, d->top_k);
+  if (ws == nullptr || ws_bytes < p.total)
+    return fail(MSA_ERR_WORKSPACE, "route workspace: need %zu bytes, got %zu", p.total, ws_bytes);
+  char* base = static_cast<char*>(ws);
+  uint16_t* qh = reinterpret_cast<uint16_t*>(base + p.off_qh);
+  uint16_t* ql = reinterpret_cast<uint16_t*>(base + p.off_ql);
+  float* S = reinterpret_cast<float*>(base + p.off_S);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(base + p.off_cand);
+  int rc = launch_qprep(QR, B * M, qh, ql, s);
+  if (rc) return rc;
+  rc = p.mfma ? launch_scan_mfma(qh, ql, p.g, KRbar, n_chunks, d->token_reduce, S, s)
+              : launch_scan_valu(qh, ql, p.g, KRbar, n_chunks, d->token_reduce, S, s);
+  if (rc) return rc;
+  return launch_doc_topk(S, p.g, n_chunks, dco, n_docs, d->token_reduce, doc_scores, accumulate,
+                         d->top_k, cand, topk_ids, topk_scores, n_sel, s);
+}
+
+int check_route_args(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
+                     const msa_bf16* KRbar, const int64_t* dco, int32_t n_docs, int64_t n_chunks,
+                     const float* doc_scores, int32_t accumulate, const int32_t* topk_ids,
+                     const float* topk_scores, const int32_t* n_sel) {
+  if (!QR || !KRbar || !dco || !doc_scores || !topk_ids || !topk_scores || !n_sel)
+    return fail(MSA_ERR_INVALID_ARG, "route: NULL pointer argument");
+  if (B < 1 || M < 1) return fail(MSA_ERR_SHAPE, "route: B=%d M=%d must be >= 1", B, M);
+  if ((int64_t)B * M > (1 << 24)) return fail(MSA_ERR_SHAPE, "route: B*M too large");
+  if (n_docs < 1) return fail(MSA_ERR_SHAPE, "route: n_docs=%d must be >= 1", n_docs);
+  if (n_chunks < n_docs || n_chunks >= ((int64_t)1 << 31))
+    return fail(MSA_ERR_SHAPE, "route: n_chunks=%lld must be in [n_docs, 2^31)",
+                (long long)n_chunks);
+  if (accumulate && d->token_reduce == MSA_TOKEN_REDUCE_MEAN)
+    return fail(MSA_ERR_UNSUPPORTED, "route: accumulate needs the MAX token reduction");
+  return MSA_OK;
+}
+
+int check_attend_args(const msa_dims* d, const msa_bf16* Q, int32_t M, const msa_bf16* K_loc,
+                      const msa_bf16* V_loc, int32_t M_loc, const msa_bf16* Kbar,
+                      const msa_bf16* Vbar, int64_t n_chunks, const int64_t* dco, int32_t n_docs,
+                      const int32_t* sel_ids, const int32_t* n_sel, int64_t max_sel_chunks,
+                      const msa_bf16* out) {
+  (void)d;
+  if (!Q || !K_loc || !V_loc || !Kbar || !Vbar || !dco || !sel_ids || !n_sel || !out)
+    return fail(MSA_ERR_INVALID_ARG, "attend: NULL pointer argument");
+  if (M < 1 || M_loc < M)
+    return fail(MSA_ERR_SHAPE, "attend: need 1 <= M (%d) <= M_loc (%d)", M, M_loc);
+  if ((int64_t)M_loc > (1 << 20)) return fail(MSA_ERR_SHAPE, "attend: M_loc too large");
+  if (n_docs < 1) return fail(MSA_ERR_SHAPE, "attend: n_docs=%d must be >= 1", n_docs);
+  if (n_chunks < n_docs || n_chunks >= ((int64_t)1 << 31))
+    return fail(MSA_ERR_SHAPE, "attend: n_chunks=%lld must be in [n_docs, 2^31)",
+                (long long)n_chunks);
+  if (max_sel_chunks < 0 || max_sel_chunks > ((int64_t)1 << 24))
+    return fail(MSA_ERR_SHAPE, "attend: max_sel_chunks=%lld out of [0, 2^24]",
+                (long long)max_sel_chunks);
+  return MSA_OK;
+}
+
+}  // namespace
+}  // namespace msa
+
+using namespace msa;
+
+extern "C" {
+
+void msa_default_dims(msa_dims* d) {
+  if (!d) return;
+  d->n_kv_heads = 8;
+  d->n_router_heads = 8;
+  d->n_q_heads = 32;
+  d->head_dim = 128;
+  d->chunk = 64;
+  d->top_k = 16;
+  d->rope_theta = 1.0e6f;
+  d->token_reduce = MSA_TOKEN_REDUCE_MAX;
+  d->doc_rope_mode = MSA_DOC_ROPE_TOKEN;
+}
+
+const char* msa_last_error(void) { return g_err; }
+
+int32_t msa_abi_version(void) { return MSA_ABI_VERSION; }
+
+int32_t msa_plan_chunks(const int64_t* dto_h, int32_t n_docs, int32_t chunk, int64_t* dco_h) {
+  clear_error();
+  if (!dto_h || !dco_h) return fail(MSA_ERR_INVALID_ARG, "plan_chunks: NULL pointer argument");
+  if (n_docs < 0) return fail(MSA_ERR_SHAPE, "plan_chunks: n_docs=%d < 0", n_docs);
+  if (chunk < 1) return fail(MSA_ERR_SHAPE, "plan_chunks: chunk=%d < 1", chunk);
+  if (dto_h[0] < 0) return fail(MSA_ERR_SHAPE, "plan_chunks: negative first offset");
+  for (int32_t i = 0; i < n_docs; ++i)
+    if (dto_h[i + 1] - dto_h[i] < 1)
+      return fail(MSA_ERR_SHAPE, "plan_chunks: document %d has %lld tokens (needs >= 1)", i,
+                  (long long)(dto_h[i + 1] - dto_h[i]));
+  int64_t acc = 0;
+  dco_h[0] = 0;
+  for (int32_t i = 0; i < n_docs; ++i) {
+    const int64_t n = dto_h[i + 1] - dto_h[i];
+    acc += (n + chunk - 1) / chunk;
+    dco_h[i + 1] = acc;
+  }
+  return MSA_OK;
+}
+
+size_t msa_encode_pool_workspace(const msa_dims* d, int32_t n_docs, int64_t n_chunks) {
+  (void)d; (void)n_docs; (void)n_chunks;
+  return 0;
+}
+
+int32_t msa_encode_pool(const msa_dims* d, const msa_bf16* K, const msa_bf16* V,
+                        const msa_bf16* KR, const int64_t* dto, const int64_t* dco, int32_t n_docs,
+                        int64_t n_tokens, int64_t n_chunks, msa_bf16* Kbar, msa_bf16* Vbar,
+                        msa_bf16* KRbar, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  (void)ws; (void)ws_bytes;
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!dto || !dco) return fail(MSA_ERR_INVALID_ARG, "encode_pool: NULL offsets");
+  if ((Kbar && !K) || (Vbar && !V) || (KRbar && !KR))
+    return fail(MSA_ERR_INVALID_ARG, "encode_pool: an output is requested without its input");
+  if (n_docs < 1) return fail(MSA_ERR_SHAPE, "encode_pool: n_docs=%d must be >= 1", n_docs);
+  if (n_tokens < n_docs) return fail(MSA_ERR_SHAPE, "encode_pool: n_tokens < n_docs");
+  if (n_chunks < n_docs || n_chunks > n_tokens)
+    return fail(MSA_ERR_SHAPE, "encode_pool: n_chunks=%lld must be in [n_docs, n_tokens]",
+                (long long)n_chunks);
+  if (n_chunks / 8 >= ((int64_t)1 << 31)) return fail(MSA_ERR_SHAPE, "encode_pool: too many chunks");
+  PoolArgs a;
+  a.K = K; a.V = V; a.KR = KR; a.dto = dto; a.dco = dco;
+  a.n_docs = n_docs; a.n_tokens = n_tokens; a.n_chunks = n_chunks; a.chunk = d->chunk;
+  a.theta = (double)d->rope_theta; a.rope_mode = d->doc_rope_mode;
+  a.Kbar = Kbar; a.Vbar = Vbar; a.KRbar = KRbar;
+  return launch_pool(a, static_cast<hipStream_t>(stream));
+}
+
+size_t msa_route_topk_workspace(const msa_dims* d, int32_t B, int32_t M, int64_t n_chunks,
+                                int32_t n_docs) {
+  if (!d || B < 1 || M < 1 || n_chunks < 1 || n_docs < 1) return 0;
+  return route_plan(B, M, n_chunks, n_docs, d->top_k).total;
+}
+
+int32_t msa_route_topk(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
+                       const msa_bf16* KRbar, const int64_t* dco, int32_t n_docs, int64_t n_chunks,
+                       float* doc_scores, int32_t accumulate, int32_t* topk_ids,
+                       float* topk_scores, int32_t* n_sel, void* ws, size_t ws_bytes,
+                       void* stream) {
+  clear_error();
+  int rc = check_dims(d);
+  if (rc) return rc;
+  rc = check_route_args(d, QR, B, M, KRbar, dco, n_docs, n_chunks, doc_scores, accumulate,
+                        topk_ids, topk_scores, n_sel);
+  if (rc) return rc;
+  return route_topk_impl(d, QR, B, M, KRbar, dco, n_docs, n_chunks, doc_scores, accumulate,
+                         topk_ids, topk_scores, n_sel, ws, ws_bytes,
+                         static_cast<hipStream_t>(stream));
+}
+
+size_t msa_sparse_attend_workspace(const msa_dims* d, int32_t M, int32_t M_loc,
+                                   int64_t max_sel_chunks) {
+  if (!d || M < 1 || M_loc < M || max_sel_chunks < 0) return 0;
+  return attend_workspace(M, M_loc, d->n_q_heads, max_sel_chunks);
+}
+
+int32_t msa_sparse_attend(const msa_dims* d, const msa_bf16* Q, int32_t M, const msa_bf16* K_loc,
+                          const msa_bf16* V_loc, int32_t M_loc, int32_t k_loc_rotated,
+                          const msa_bf16* Kbar, const msa_bf16* Vbar, int32_t kv_on_host,
+                          int64_t n_chunks, const int64_t* dco, int32_t n_docs,
+                          const int32_t* sel_ids, const int32_t* n_sel, int64_t max_sel_chunks,
+                          int64_t pos0, msa_bf16* out, float* out_f32, void* ws, size_t ws_bytes,
+                          void* stream) {
+  clear_error();
+  int rc = check_dims(d);
+  if (rc) return rc;
+  rc = check_attend_args(d, Q, M, K_loc, V_loc, M_loc, Kbar, Vbar, n_chunks, dco, n_docs, sel_ids,
+                         n_sel, max_sel_chunks, out);
+  if (rc) return rc;
+  const size_t need = attend_workspace(M, M_loc, d->n_q_heads, max_sel_chunks);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "attend workspace: need %zu bytes, got %zu", need, ws_bytes);
+  const void* kb = nullptr;
+  const void* vb = nullptr;
+  rc = resolve_kv(Kbar, kv_on_host, &kb, "Kbar");
+  if (rc) return rc;
+  rc = resolve_kv(Vbar, kv_on_host, &vb, "Vbar");
+  if (rc) return rc;
+  AttendArgs a;
+  a.Q = Q; a.M = M; a.n_q_heads = d->n_q_heads;
+  a.K_loc = K_loc; a.V_loc = V_loc; a.M_loc = M_loc; a.k_loc_rotated = k_loc_rotated;
+  a.Kbar = static_cast<const uint16_t*>(kb); a.Vbar = static_cast<const uint16_t*>(vb);
+  a.n_chunks = n_chunks; a.dco = dco; a.n_docs = n_docs;
+  a.sel_ids = sel_ids; a.n_sel = n_sel; a.top_k = d->top_k;
+  a.max_sel_chunks = max_sel_chunks; a.pos0 = pos0; a.theta = (double)d->rope_theta;
+  a.out = out; a.out_f32 = out_f32;
+  return launch_attend(a, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int32_t msa_interleave_reset(msa_interleave_state* st, int32_t n_docs, void* stream) {
+  clear_error();
+  if (!st || !st->doc_scores) return fail(MSA_ERR_INVALID_ARG, "interleave_reset: NULL state");
+  if (n_docs < 1) return fail(MSA_ERR_SHAPE, "interleave_reset: n_docs=%d must be >= 1", n_docs);
+  int rc = launch_fill_f32(st->doc_scores, n_docs, -INFINITY, static_cast<hipStream_t>(stream));
+  if (rc) return rc;
+  st->n_loc = 0;
+  return MSA_OK;
+}
+
+size_t msa_interleave_step_workspace(const msa_dims* d, int32_t M_new, int32_t cap_loc,
+                                     int64_t n_chunks, int32_t n_docs, int64_t max_sel_chunks) {
+  if (!d || M_new < 1 || cap_loc < M_new || n_chunks < 1 || n_docs < 1 || max_sel_chunks < 0)
+    return 0;
+  const size_t r = route_plan(1, M_new, n_chunks, n_docs, d->top_k).total;
+  const size_t a = attend_workspace(M_new, cap_loc, d->n_q_heads, max_sel_chunks);
+  return r > a ? r : a;
+}
+
+int32_t msa_interleave_step(const msa_dims* d, msa_interleave_state* st, const msa_bf16* Q_new,
+                            const msa_bf16* K_new, const msa_bf16* V_new, const msa_bf16* QR_new,
+                            int32_t M_new, const msa_bf16* KRbar, const msa_bf16* Kbar,
+                            const msa_bf16* Vbar, int32_t kv_on_host, int64_t n_chunks,
+                            const int64_t* dco, int32_t n_docs, int64_t max_sel_chunks,
+                            msa_bf16* out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!st || !st->doc_scores || !st->K_loc || !st->V_loc || !st->topk_ids || !st->topk_scores ||
+      !st->n_sel)
+    return fail(MSA_ERR_INVALID_ARG, "interleave: NULL state buffer");
+  if (!Q_new || !K_new || !V_new || !QR_new)
+    return fail(MSA_ERR_INVALID_ARG, "interleave: NULL input");
+  if (M_new < 1 || st->n_loc < 0 || (int64_t)st->n_loc + M_new > st->cap_loc)
+    return fail(MSA_ERR_SHAPE, "interleave: n_loc (%d) + M_new (%d) exceeds cap_loc (%d)",
+                st->n_loc, M_new, st->cap_loc);
+  rc = check_route_args(d, QR_new, 1, M_new, KRbar, dco, n_docs, n_chunks, st->doc_scores, 1,
+                        st->topk_ids, st->topk_scores, st->n_sel);
+  if (rc) return rc;
+  const int32_t M_loc = st->n_loc + M_new;
+  rc = check_attend_args(d, Q_new, M_new, st->K_loc, st->V_loc, M_loc, Kbar, Vbar, n_chunks, dco,
+                         n_docs, st->topk_ids, st->n_sel, max_sel_chunks, out);
+  if (rc) return rc;
+  const size_t need_r = route_plan(1, M_new, n_chunks, n_docs, d->top_k).total;
+  const size_t need_a = attend_workspace(M_new, M_loc, d->n_q_heads, max_sel_chunks);
+  if (ws == nullptr || ws_bytes < need_r || ws_bytes < need_a)
+    return fail(MSA_ERR_WORKSPACE, "interleave workspace too small");
+  const void* kb = nullptr;
+  const void* vb = nullptr;
+  rc = resolve_kv(Kbar, kv_on_host, &kb, "Kbar");
+  if (rc) return rc;
+  rc = resolve_kv(Vbar, kv_on_host, &vb, "Vbar");
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  rc = route_topk_impl(d, QR_new, 1, M_new, KRbar, dco, n_docs, n_chunks, st->doc_scores, 1,
+                       st->topk_ids, st->topk_scores, st->n_sel, ws, ws_bytes, s);
+  if (rc) return rc;
+  const size_t row_bytes = (size_t)kRowElems * 2;
+  MSA_HIP(hipMemcpyAsync(st->K_loc + (size_t)st->n_loc * kRowElems, K_new, row_bytes * M_new,
+                         hipMemcpyDeviceToDevice, s));
+  MSA_HIP(hipMemcpyAsync(st->V_loc + (size_t)st->n_loc * kRowElems, V_new, row_bytes * M_new,
+                         hipMemcpyDeviceToDevice, s));
+  AttendArgs a;
+  a.Q = Q_new; a.M = M_new; a.n_q_heads = d->n_q_heads;
+  a.K_loc = st->K_loc; a.V_loc = st->V_loc; a.M_loc = M_loc; a.k_loc_rotated = 0;
+  a.Kbar = static_cast<const uint16_t*>(kb); a.Vbar = static_cast<const uint16_t*>(vb);
+  a.n_chunks = n_chunks; a.dco = dco; a.n_docs = n_docs;
+  a.sel_ids = st->topk_ids; a.n_sel = st->n_sel; a.top_k = d->top_k;
+  a.max_sel_chunks = max_sel_chunks; a.pos0 = st->pos0; a.theta = (double)d->rope_theta;
+  a.out = out; a.out_f32 = nullptr;
+  rc = launch_attend(a, ws, ws_bytes, s);
+  if (rc) return rc;
+  st->n_loc = M_loc;
+  return MSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,412 @@
+// msa_gather_attend: context assembly, global RoPE and sparse attention
+// (MSA stage 3).
+//
+// Method (portal.techblg.uk IRMaD reading, section M, routing bullet and
+// positional-encoding bullet):
+//   K_ctx = [{K̄_i}_{i∈I}; K_q],  V_ctx = [{V̄_i}_{i∈I}; V_q],
+//   Output = Attention(Q_q, K_ctx, V_ctx),
+// and the active context (query and generated tokens) carries global RoPE with
+// positions offset from k (also zhichai.net "关键技术细节" 1, chooseai.io 2.2).
+// Readings: local token v sits at pos0 + v with pos0 = n_sel by default; the
+// M query tokens are the last M local tokens; memory chunks are fully visible
+// and local keys causal; logits scale 1/sqrt(128); q head h reads KV head
+// h / (Hq / 8); memory chunks enter in rank order.
+//
+// Pipeline (one stream, four launches):
+//   assemble  (1 wave)   selected ids -> list of memory chunk rows, n_mem,
+//                        resolved pos0;
+//   rope      (elementwise) Q and K_loc rotated once into the workspace (bf16);
+//   attn      (MFMA)     flash attention, one wave per (32 query rows of one KV
+//                        group, KV head, key split): S = Q·K^T with
+//                        v_mfma_f32_32x32x16_bf16 (K fragments loaded straight
+//                        from memory — 16 contiguous bytes per lane), online
+//                        softmax in fp32 (exp2 domain), P re-laid out through
+//                        LDS, V staged transposed in LDS so its MFMA fragments
+//                        are 16-byte LDS reads, O += P·V. Memory rows are read
+//                        in place, from HBM or from pinned host memory over
+//                        PCIe (no staging copy);
+//   combine              merges the key splits (log-sum-exp) and writes bf16
+//                        (and optionally fp32) output.
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kKeyTile = 32;
+constexpr int kRowTile = 32;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnWs {
+  int32_t* mem_rows;   // [max_sel_chunks]
+  int32_t* n_mem;      // [1]
+  int64_t* pos0;       // [1]
+  uint16_t* Qr;        // [M][Hq][128]
+  uint16_t* Kr;        // [M_loc][8][128]
+  float* Opart;        // [n_splits][M*Hq][128]
+  float* ML;           // [n_splits][M*Hq][2]
+};
+
+__global__ __launch_bounds__(64) void assemble_kernel(const int32_t* __restrict__ sel_ids,
+                                                      const int32_t* __restrict__ n_sel_p,
+                                                      int32_t top_k,
+                                                      const int64_t* __restrict__ dco,
+                                                      int32_t n_docs, int64_t n_chunks,
+                                                      int64_t max_sel, int64_t pos0_in,
+                                                      int32_t* __restrict__ mem_rows,
+                                                      int32_t* __restrict__ n_mem,
+                                                      int64_t* __restrict__ pos0_out) {
+  const int lane = threadIdx.x;
+  int ns = *n_sel_p;
+  ns = ns < 0 ? 0 : (ns > top_k ? top_k : ns);
+  int64_t start = 0, cnt = 0;
+  if (lane < ns) {
+    const int32_t id = sel_ids[lane];
+    if (id >= 0 && id < n_docs) {
+      int64_t c0 = dco[id], c1 = dco[id + 1];
+      c0 = max((int64_t)0, min(c0, n_chunks));
+      c1 = max(c0, min(c1, n_chunks));
+      start = c0;
+      cnt = c1 - c0;
+    }
+  }
+  // exclusive prefix sum of cnt over the wave
+  int64_t incl = cnt;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  const int64_t off = incl - cnt;
+  const int64_t total = __shfl(incl, 63);
+  for (int64_t j = 0; j < cnt && off + j < max_sel; ++j) mem_rows[off + j] = (int32_t)(start + j);
+  if (lane == 0) {
+    *n_mem = (int32_t)(total < max_sel ? total : max_sel);
+    *pos0_out = pos0_in < 0 ? (int64_t)ns : pos0_in;
+  }
+}
+
+// Rotates Q (rows u·Hq + h, position pos0 + M_loc − M + u) and, unless the
+// caller did, K_loc (rows v·8 + g, position pos0 + v). One thread per pair.
+__global__ __launch_bounds__(256) void rope_kernel(const uint16_t* __restrict__ Q, int32_t M,
+                                                   int32_t Hq, const uint16_t* __restrict__ Kl,
+                                                   int32_t M_loc, int32_t rotate_k, double theta,
+                                                   const int64_t* __restrict__ pos0_p,
+                                                   uint16_t* __restrict__ Qr,
+                                                   uint16_t* __restrict__ Kr) {
+  const int64_t q_pairs = (int64_t)M * Hq * 64;
+  const int64_t k_pairs = rotate_k ? (int64_t)M_loc * kHeads * 64 : 0;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= q_pairs + k_pairs) return;
+  const int64_t pos0 = *pos0_p;
+  const uint16_t* src;
+  uint16_t* dst;
+  int64_t pos;
+  int m;
+  if (idx < q_pairs) {
+    const int64_t row = idx / 64;  // u * Hq + h
+    m = (int)(idx % 64);
+    const int64_t u = row / Hq;
+    pos = pos0 + (M_loc - M) + u;
+    src = Q + row * kDim;
+    dst = Qr + row * kDim;
+  } else {
+    const int64_t k = idx - q_pairs;
+    const int64_t row = k / 64;  // v * 8 + g
+    m = (int)(k % 64);
+    pos = pos0 + row / kHeads;
+    src = Kl + row * kDim;
+    dst = Kr + row * kDim;
+  }
+  const double om = pow(theta, -2.0 * (double)m / (double)kDim);
+  double s, c;
+  sincos((double)pos * om, &s, &c);
+  const double x = bf16f(src[m]), y = bf16f(src[m + 64]);
+  dst[m] = d2bf(x * c - y * s);
+  dst[m + 64] = d2bf(y * c + x * s);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// LDS pitches (bf16 elements): P tile [32 rows][32 keys], V^T tile [128][32].
+constexpr int kPPitch = 40;
+constexpr int kVPitch = 40;
+
+__global__ __launch_bounds__(64) void attn_kernel(const uint16_t* __restrict__ Qr, int32_t M,
+                                                  int32_t Hq, const uint16_t* __restrict__ Kloc,
+                                                  const uint16_t* __restrict__ Vloc,
+                                                  int32_t M_loc, const uint16_t* Kbar,
+                                                  const uint16_t* Vbar,
+                                                  const int32_t* __restrict__ mem_rows,
+                                                  const int32_t* __restrict__ n_mem_p,
+                                                  int32_t key_split, float qk_scale_log2,
+                                                  float* __restrict__ Opart,
+                                                  float* __restrict__ ML) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[kRowTile * kPPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kDim * kVPitch];
+
+  const int lane = threadIdx.x;
+  const int col = lane & 31;      // MFMA column lane (key / dim)
+  const int half = lane >> 5;     // which 8-wide k slice this lane holds
+  const int rb = blockIdx.x;      // row block within the KV group
+  const int g = blockIdx.y;       // KV head
+  const int split = blockIdx.z;
+  const int G = Hq / kHeads;      // query heads per KV head
+  const int rows_g = M * G;
+  const int n_mem = *n_mem_p;
+  const int n_keys = n_mem + M_loc;
+  const int k_begin = split * key_split;
+  const int k_end = min(k_begin + key_split, n_keys);
+  const int64_t n_rows_tot = (int64_t)M * Hq;
+
+  // A fragments of this lane's query row (row = l % 32 of the block).
+  uint4 qa[8];
+  {
+    const int r = rb * kRowTile + col;
+    if (r < rows_g) {
+      const int u = r / G, h = g * G + r % G;
+      const uint4* qrow = reinterpret_cast<const uint4*>(Qr + ((int64_t)u * Hq + h) * kDim);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) qa[ks] = qrow[ks * 2 + half];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) qa[ks] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  // The 16 accumulator rows this lane holds: i(v) = 8(v/4) + 4·half + v%4.
+  int u_of[16];
+  bool row_ok[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int r = rb * kRowTile + 8 * (v >> 2) + 4 * half + (v & 3);
+    row_ok[v] = r < rows_g;
+    u_of[v] = r / G;
+  }
+
+  f32x16_t O[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) O[db][v] = 0.0f;
+  float mrow[16], lpart[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) { mrow[v] = -INFINITY; lpart[v] = 0.0f; }
+
+  for (int kt = k_begin; kt < k_end; kt += kKeyTile) {
+    // ---- K fragments straight from memory: key kt + col, 16 bytes per k-step
+    uint4 kb[8];
+    {
+      const int j = kt + col;
+      const uint16_t* krow = nullptr;
+      if (j < k_end) {
+        krow = j < n_mem ? Kbar + ((int64_t)mem_rows[j] * kHeads + g) * kDim
+                         : Kloc + ((int64_t)(j - n_mem) * kHeads + g) * kDim;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        kb[ks] = krow ? reinterpret_cast<const uint4*>(krow)[ks * 2 + half] : make_uint4(0, 0, 0, 0);
+    }
+    // ---- V tile -> LDS, transposed to [dim][key]
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int idx = it * 64 + lane;  // 512 vectors of 8 dims
+      const int kk = idx >> 4, dv = idx & 15;
+      const int j = kt + kk;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (j < k_end) {
+        const uint16_t* vrow = j < n_mem ? Vbar + ((int64_t)mem_rows[j] * kHeads + g) * kDim
+                                         : Vloc + ((int64_t)(j - n_mem) * kHeads + g) * kDim;
+        x = reinterpret_cast<const uint4*>(vrow)[dv];
+      }
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Vt[(dv * 8 + 2 * e) * kVPitch + kk] = (uint16_t)(w[e] & 0xffffu);
+        Vt[(dv * 8 + 2 * e + 1) * kVPitch + kk] = (uint16_t)(w[e] >> 16);
+      }
+    }
+
+    // ---- S = Q K^T (rows × 32 keys)
+    f32x16_t S;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) S[v] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[ks]), as_bf16x8(kb[ks]), S, 0, 0, 0);
+
+    // ---- mask, scale to the log2 domain, online softmax
+    const int j = kt + col;
+    const bool key_ok = j < k_end;
+    const int vloc = j - n_mem;  // local index when j >= n_mem
+    float p[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      bool ok = key_ok && row_ok[v] && (j < n_mem || vloc <= (M_loc - M) + u_of[v]);
+      float s = ok ? S[v] * qk_scale_log2 : -INFINITY;
+      float t = s;
+      t = fmaxf(t, __shfl_xor(t, 1));
+      t = fmaxf(t, __shfl_xor(t, 2));
+      t = fmaxf(t, __shfl_xor(t, 4));
+      t = fmaxf(t, __shfl_xor(t, 8));
+      t = fmaxf(t, __shfl_xor(t, 16));
+      const float mn = fmaxf(mrow[v], t);
+      const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(mrow[v] - mn);
+      p[v] = (mn == -INFINITY) ? 0.0f : exp2f(s - mn);
+      lpart[v] = lpart[v] * alpha + p[v];
+      mrow[v] = mn;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) O[db][v] *= alpha;
+    }
+    // ---- P -> LDS [row][key] as bf16, then A fragments (16 keys per k-step)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int i = 8 * (v >> 2) + 4 * half + (v & 3);
+      Ps[i * kPPitch + col] = f2bf(p[v]);
+    }
+    __syncthreads();
+    uint4 pa[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+      pa[k2] = *reinterpret_cast<const uint4*>(&Ps[col * kPPitch + k2 * 16 + half * 8]);
+    // ---- O += P V : B fragment = 8 keys of one dim, contiguous in V^T
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const uint4 vb =
+            *reinterpret_cast<const uint4*>(&Vt[(db * 32 + col) * kVPitch + k2 * 16 + half * 8]);
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pa[k2]), as_bf16x8(vb), O[db],
+                                                        0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- row sums of p over the 32 key lanes, then write the partials
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float t = lpart[v];
+    t += __shfl_xor(t, 1);
+    t += __shfl_xor(t, 2);
+    t += __shfl_xor(t, 4);
+    t += __shfl_xor(t, 8);
+    t += __shfl_xor(t, 16);
+    lpart[v] = t;
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    if (!row_ok[v]) continue;
+    const int r = rb * kRowTile + 8 * (v >> 2) + 4 * half + (v & 3);
+    const int u = r / G, h = g * G + r % G;
+    const int64_t grow = (int64_t)split * n_rows_tot + (int64_t)u * Hq + h;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) Opart[grow * kDim + db * 32 + col] = O[db][v];
+    if (col == 0) {
+      ML[grow * 2] = mrow[v];
+      ML[grow * 2 + 1] = lpart[v];
+    }
+  }
+}
+
+__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ Opart,
+                                                      const float* __restrict__ ML,
+                                                      int32_t n_splits, int64_t n_rows,
+                                                      uint16_t* __restrict__ out,
+                                                      float* __restrict__ out_f32) {
+  const int64_t row = blockIdx.x;
+  const int d = threadIdx.x;
+  float mx = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, ML[((int64_t)s * n_rows + row) * 2]);
+  float L = 0.0f, acc = 0.0f;
+  if (mx != -INFINITY) {
+    for (int s = 0; s < n_splits; ++s) {
+      const float m = ML[((int64_t)s * n_rows + row) * 2];
+      if (m == -INFINITY) continue;
+      const float w = exp2f(m - mx);
+      L += w * ML[((int64_t)s * n_rows + row) * 2 + 1];
+      acc += w * Opart[((int64_t)s * n_rows + row) * kDim + d];
+    }
+  }
+  const float o = L > 0.0f ? acc / L : 0.0f;
+  out[row * kDim + d] = f2bf(o);
+  if (out_f32) out_f32[row * kDim + d] = o;
+}
+
+struct AttnPlan {
+  int32_t row_blocks, key_split, n_splits;
+  size_t off_rows, off_nmem, off_pos0, off_qr, off_kr, off_opart, off_ml, total;
+};
+
+AttnPlan attn_plan(int32_t M, int32_t M_loc, int32_t Hq, int64_t max_sel) {
+  AttnPlan p;
+  const int32_t G = Hq / kHeads;
+  p.row_blocks = (M * G + kRowTile - 1) / kRowTile;
+  const int64_t max_keys = max_sel + M_loc;
+  // aim for >= 512 waves in flight across the chip
+  int64_t want = 512 / ((int64_t)p.row_blocks * kHeads);
+  if (want < 1) want = 1;
+  int64_t tiles = (max_keys + kKeyTile - 1) / kKeyTile;
+  int64_t tiles_per_split = (tiles + want - 1) / want;
+  if (tiles_per_split < 1) tiles_per_split = 1;
+  p.key_split = (int32_t)(tiles_per_split * kKeyTile);
+  p.n_splits = (int32_t)((max_keys + p.key_split - 1) / p.key_split);
+  if (p.n_splits < 1) p.n_splits = 1;
+  size_t o = 0;
+  p.off_rows = o; o = align_up(o + sizeof(int32_t) * (size_t)(max_sel > 0 ? max_sel : 1), 256);
+  p.off_nmem = o; o = align_up(o + sizeof(int32_t), 256);
+  p.off_pos0 = o; o = align_up(o + sizeof(int64_t), 256);
+  p.off_qr = o; o = align_up(o + 2 * (size_t)M * Hq * kDim, 256);
+  p.off_kr = o; o = align_up(o + 2 * (size_t)M_loc * kHeads * kDim, 256);
+  p.off_opart = o; o = align_up(o + 4 * (size_t)p.n_splits * M * Hq * kDim, 256);
+  p.off_ml = o; o = align_up(o + 4 * 2 * (size_t)p.n_splits * M * Hq, 256);
+  p.total = o;
+  return p;
+}
+
+}  // namespace
+
+size_t attend_workspace(int32_t M, int32_t M_loc, int32_t n_q_heads, int64_t max_sel_chunks) {
+  return attn_plan(M, M_loc, n_q_heads, max_sel_chunks).total;
+}
+
+int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
+  const AttnPlan p = attn_plan(a.M, a.M_loc, a.n_q_heads, a.max_sel_chunks);
+  if (ws_bytes < p.total) return fail(MSA_ERR_WORKSPACE, "attend workspace too small");
+  char* base = static_cast<char*>(ws);
+  AttnWs w;
+  w.mem_rows = reinterpret_cast<int32_t*>(base + p.off_rows);
+  w.n_mem = reinterpret_cast<int32_t*>(base + p.off_nmem);
+  w.pos0 = reinterpret_cast<int64_t*>(base + p.off_pos0);
+  w.Qr = reinterpret_cast<uint16_t*>(base + p.off_qr);
+  w.Kr = reinterpret_cast<uint16_t*>(base + p.off_kr);
+  w.Opart = reinterpret_cast<float*>(base + p.off_opart);
+  w.ML = reinterpret_cast<float*>(base + p.off_ml);
+
+  hipLaunchKernelGGL(assemble_kernel, dim3(1), dim3(64), 0, s, a.sel_ids, a.n_sel, a.top_k, a.dco,
+                     a.n_docs, a.n_chunks, a.max_sel_chunks, a.pos0, w.mem_rows, w.n_mem, w.pos0);
+  MSA_LAUNCH_CHECK("assemble_kernel launch");
+
+  const int rotate_k = a.k_loc_rotated ? 0 : 1;
+  const int64_t pairs = (int64_t)a.M * a.n_q_heads * 64 + (rotate_k ? (int64_t)a.M_loc * kHeads * 64 : 0);
+  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s, a.Q, a.M,
+                     a.n_q_heads, a.K_loc, a.M_loc, rotate_k, a.theta, w.pos0, w.Qr, w.Kr);
+  MSA_LAUNCH_CHECK("rope_kernel launch");
+
+  const uint16_t* kloc = rotate_k ? w.Kr : a.K_loc;
+  const float scale = (float)(1.0 / sqrt((double)kDim)) * kLog2e;
+  hipLaunchKernelGGL(attn_kernel, dim3(p.row_blocks, kHeads, p.n_splits), dim3(64), 0, s, w.Qr,
+                     a.M, a.n_q_heads, kloc, a.V_loc, a.M_loc, a.Kbar, a.Vbar, w.mem_rows, w.n_mem,
+                     p.key_split, scale, w.Opart, w.ML);
+  MSA_LAUNCH_CHECK("attn_kernel launch");
+
+  const int64_t n_rows = (int64_t)a.M * a.n_q_heads;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)n_rows), dim3(kDim), 0, s, w.Opart, w.ML,
+                     p.n_splits, n_rows, a.out, a.out_f32);
+  MSA_LAUNCH_CHECK("combine_kernel launch");
+  return MSA_OK;
+}
+
+}  // namespace msa

@@ -1,0 +1,155 @@
+// Internal declarations shared by the MSA HIP sources: error reporting,
+// bf16 conversions, wave-level helpers and the kernel launchers that the C
+// entry points in msa_api.hip call. Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "msa.h"
+
+namespace msa {
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+int hip_fail(hipError_t e, const char* what);
+
+#define MSA_HIP(expr)                                   \
+  do {                                                  \
+    hipError_t e_ = (expr);                             \
+    if (e_ != hipSuccess) return ::msa::hip_fail(e_, #expr); \
+  } while (0)
+
+#define MSA_LAUNCH_CHECK(what)                          \
+  do {                                                  \
+    hipError_t e_ = hipGetLastError();                  \
+    if (e_ != hipSuccess) return ::msa::hip_fail(e_, what); \
+  } while (0)
+
+static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Fixed head geometry of this build: 8 KV/router heads of dimension 128, so a
+// token row of one tensor is 1024 bf16 = 2 KiB = 128 × 16-byte vectors.
+constexpr int kHeads = 8;
+constexpr int kDim = 128;
+constexpr int kRowElems = kHeads * kDim;      // 1024
+constexpr int kRowVec = kRowElems / 8;        // 128 uint4 per row
+constexpr float kNormEps = 1e-6f;
+
+// ---------------------------------------------------------------------------
+// bf16 helpers (device)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// float -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// double -> bf16 with a single rounding (nearest even): first narrow to float
+// rounding toward zero and make the result odd if it was inexact ("round to
+// odd"), then round that float to bf16. Float keeps 24 bits, more than bf16's
+// 8 + 2, so the two steps round exactly once.
+__device__ __forceinline__ uint16_t d2bf(double x) {
+  if (x != x) return 0x7fc0u;
+  float f = __double2float_rz(x);
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != x && (u & 0x7fffffffu) < 0x7f800000u) u |= 1u;
+  return f2bf(__uint_as_float(u));
+}
+
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
+  return (uint32_t)lo | ((uint32_t)hi << 16);
+}
+
+// Streaming 16-byte load that is not expected to be reused (non-temporal).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Order-preserving map of a float onto uint32 (larger float -> larger key).
+// NaN maps to 0 (ranks below every number); -0 is treated as +0.
+__device__ __forceinline__ uint32_t ord_key(float f) {
+  if (f != f) return 0u;
+  if (f == 0.0f) f = 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord_val(uint32_t k) {
+  if (k == 0u) return __uint_as_float(0x7fc00000u);
+  return (k & 0x80000000u) ? __uint_as_float(k & 0x7fffffffu) : __uint_as_float(~k);
+}
+
+// NaN-propagating max (matches numpy's max / maximum).
+__device__ __forceinline__ float nan_max(float a, float b) {
+  if (a != a) return a;
+  if (b != b) return b;
+  return b > a ? b : a;
+}
+
+// ---------------------------------------------------------------------------
+// launchers (each returns MSA_OK or a negative status)
+// ---------------------------------------------------------------------------
+struct PoolArgs {
+  const uint16_t* K; const uint16_t* V; const uint16_t* KR;
+  const int64_t* dto; const int64_t* dco;
+  int32_t n_docs; int64_t n_tokens; int64_t n_chunks; int32_t chunk;
+  double theta; int32_t rope_mode;
+  uint16_t* Kbar; uint16_t* Vbar; uint16_t* KRbar;
+};
+int launch_pool(const PoolArgs& a, hipStream_t s);
+
+// Router-query preparation + chunk scan. The chunk scores are reduced over
+// the query tokens inside one row tile; S holds [parts][B][C] fp32.
+struct RouteGeom {
+  int32_t B, M;           // queries, tokens per query
+  int32_t tile_rows;      // rows per tile (kernel dependent)
+  int32_t q_per_tile;     // whole queries per tile (M <= tile_rows) else 1
+  int32_t parts;          // tiles per query (M > tile_rows) else 1
+  int32_t n_tiles;        // row tiles in the grid
+};
+RouteGeom route_geom(int32_t B, int32_t M, int32_t tile_rows);
+int launch_qprep(const uint16_t* QR, int32_t rows, uint16_t* q_hi, uint16_t* q_lo, hipStream_t s);
+int launch_scan_valu(const uint16_t* q_hi, const uint16_t* q_lo, const RouteGeom& g,
+                     const uint16_t* KRbar, int64_t n_chunks, int32_t token_reduce,
+                     float* S, hipStream_t s);
+int launch_scan_mfma(const uint16_t* q_hi, const uint16_t* q_lo, const RouteGeom& g,
+                     const uint16_t* KRbar, int64_t n_chunks, int32_t token_reduce,
+                     float* S, hipStream_t s);
+constexpr int kValuTileRows = 8;
+constexpr int kMfmaTileRows = 64;
+
+// Doc reduce + top-k.
+constexpr int kTopkSlice = 1024;   // documents per stage-1 workgroup
+int launch_doc_topk(const float* S, const RouteGeom& g, int64_t n_chunks,
+                    const int64_t* dco, int32_t n_docs, int32_t token_reduce,
+                    float* doc_scores, int32_t accumulate, int32_t top_k,
+                    uint64_t* cand, int32_t* topk_ids, float* topk_scores, int32_t* n_sel,
+                    hipStream_t s);
+int launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+
+// Sparse attention.
+struct AttendArgs {
+  const uint16_t* Q; int32_t M; int32_t n_q_heads;
+  const uint16_t* K_loc; const uint16_t* V_loc; int32_t M_loc; int32_t k_loc_rotated;
+  const uint16_t* Kbar; const uint16_t* Vbar; int64_t n_chunks;
+  const int64_t* dco; int32_t n_docs;
+  const int32_t* sel_ids; const int32_t* n_sel; int32_t top_k;
+  int64_t max_sel_chunks; int64_t pos0; double theta;
+  uint16_t* out; float* out_f32;
+};
+size_t attend_workspace(int32_t M, int32_t M_loc, int32_t n_q_heads, int64_t max_sel_chunks);
+int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
+
+}  // namespace msa

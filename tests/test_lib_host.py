@@ -1,0 +1,93 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every symbol that
+include/msa.h declares, and its host logic (chunk plan, argument validation,
+workspace sizing) behaves as documented. No GPU compute is launched here:
+every validation case below fails before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import routed_sparse_attention_amd as msa
+from oracle import msa_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "msa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(msa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = msa.lib()
+    for name in _declared():
+        assert hasattr(L, name), f"libmsa.so does not export {name}"
+    assert L.msa_abi_version() == 1
+
+
+def test_default_dims_follow_the_pages():
+    d = msa.dims()
+    assert (d.n_kv_heads, d.n_router_heads, d.head_dim, d.chunk, d.top_k) == \
+        (O.N_KV_HEADS, O.N_ROUTER_HEADS, O.HEAD_DIM, O.CHUNK, O.TOP_K)
+    assert d.n_q_heads == 32 and d.rope_theta == 1e6 and d.token_reduce == 0 and d.doc_rope_mode == 0
+
+
+def test_plan_chunks_matches_oracle():
+    rng = np.random.default_rng(3)
+    for chunk in (1, 7, 64, 100):
+        lengths = rng.integers(1, 500, size=200)
+        offs = np.concatenate([[0], np.cumsum(lengths)])
+        assert np.array_equal(msa.plan_chunks(offs, chunk), O.plan_chunks(offs, chunk))
+
+
+def test_plan_chunks_rejects_empty_document():
+    with pytest.raises(msa.MsaError) as e:
+        msa.plan_chunks(np.array([0, 3, 3, 9]))
+    assert e.value.code == -2 and "document 1" in str(e.value)
+
+
+def _route(d, B=1, M=1, n_docs=4, n_chunks=8, ptr=16, accumulate=0, ws_bytes=0):
+    L = msa.lib()
+    p = ctypes.c_void_p(ptr)
+    return L.msa_route_topk(ctypes.byref(d), p, B, M, p, p, n_docs, n_chunks, p, accumulate, p, p, p,
+                            p, ws_bytes, None)
+
+
+def test_validation_codes():
+    L = msa.lib()
+    assert _route(msa.dims(head_dim=64)) == -5
+    assert b"head_dim" in L.msa_last_error()
+    assert _route(msa.dims(n_q_heads=30)) == -2
+    assert _route(msa.dims(top_k=0)) == -2
+    assert _route(msa.dims(token_reduce=3)) == -1
+    assert _route(msa.dims(rope_theta=float("nan"))) == -1
+    assert _route(msa.dims(), B=0) == -2
+    assert _route(msa.dims(), n_docs=9, n_chunks=8) == -2
+    assert _route(msa.dims(), ptr=0) == -1
+    assert _route(msa.dims(token_reduce=1), accumulate=1) == -5
+    assert _route(msa.dims(), ws_bytes=0) == -3       # the workspace check precedes any launch
+    d = msa.dims()
+    p = ctypes.c_void_p(16)
+    rc = L.msa_sparse_attend(ctypes.byref(d), p, 5, p, p, 4, 0, p, p, 0, 8, p, 2, p, p, 8, -1, p,
+                             None, p, 1 << 30, None)
+    assert rc == -2 and b"M_loc" in L.msa_last_error()
+    rc = L.msa_encode_pool(ctypes.byref(d), p, p, p, p, p, 3, 2, 3, p, p, p, None, 0, None)
+    assert rc == -2
+    rc = L.msa_encode_pool(ctypes.byref(d), None, p, p, p, p, 1, 2, 1, p, None, None, None, 0, None)
+    assert rc == -1
+
+
+def test_workspace_sizes():
+    d = msa.dims()
+    a = msa.route_topk_workspace(1, 1, 1_562_500, 46_000, d)
+    b = msa.route_topk_workspace(64, 1, 250_000, 7_350, d)
+    assert a > 1_562_500 * 4 and b > 64 * 250_000 * 4
+    assert msa.sparse_attend_workspace(1, 129, 1024, d) > 0
+    assert msa.lib().msa_route_topk_workspace(ctypes.byref(d), 0, 1, 10, 2) == 0
