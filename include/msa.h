@@ -76,7 +76,7 @@ enum { MSA_DOC_ROPE_TOKEN = 0, MSA_DOC_ROPE_CHUNK = 1 };
  * doc_rope_mode: TOKEN rotates raw K at its document-local token position
  *   before pooling; CHUNK rotates the pooled chunk at its chunk index.
  * Supported: head_dim == 128, n_kv_heads == n_router_heads == 8,
- *   n_q_heads a multiple of n_kv_heads (<= 64), chunk in [1, 64],
+ *   n_q_heads a multiple of n_kv_heads (<= 64), chunk in [1, 4096],
  *   top_k in [1, 64]. */
 typedef struct msa_dims {
   int32_t n_kv_heads;
@@ -98,7 +98,7 @@ const char* msa_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
 int32_t msa_abi_version(void);
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 
 /* ------------------------------------------------------------------------ */
 /* Chunk plan (host, pure). Each document is cut into ceil(n_i / chunk)
@@ -154,6 +154,27 @@ int32_t msa_route_topk(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t
                        int64_t n_chunks, float* doc_scores, int32_t accumulate, int32_t* topk_ids,
                        float* topk_scores, int32_t* n_sel, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* The two halves of msa_route_topk, for callers that want the chunk scores
+ * themselves (for instance to supervise routing) or to time the scan alone.
+ * msa_route_scores: chunk_scores [B, n_chunks] fp32 (written) holds
+ *   S_c = max_t (or mean_t) mean_h cos(Q^R_{t,h}, K̄^R_{c,h}) for each query.
+ *   Workspace: msa_route_scores_workspace() bytes (0 when every query's tokens
+ *   fit one row tile; then ws may be NULL).
+ * msa_select_topk: reduces chunk_scores [B, n_chunks] to document scores
+ *   (max over each document's chunks; max-merged into doc_scores when
+ *   accumulate != 0) and selects the top_k documents exactly as
+ *   msa_route_topk does. Workspace: msa_select_topk_workspace() bytes. */
+size_t msa_route_scores_workspace(const msa_dims* d, int32_t B, int32_t M, int64_t n_chunks);
+int32_t msa_route_scores(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
+                         const msa_bf16* KRbar, int64_t n_chunks, float* chunk_scores, void* ws,
+                         size_t ws_bytes, void* stream);
+size_t msa_select_topk_workspace(const msa_dims* d, int32_t B, int32_t n_docs);
+int32_t msa_select_topk(const msa_dims* d, const float* chunk_scores, int32_t B,
+                        const int64_t* doc_chunk_offsets, int32_t n_docs, int64_t n_chunks,
+                        float* doc_scores, int32_t accumulate, int32_t* topk_ids,
+                        float* topk_scores, int32_t* n_sel, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Stage 3: context assembly, global RoPE and sparse attention (techblg

@@ -9,5 +9,5 @@ RoPE, GQA attention) and ``Interleave`` (Memory Interleave rounds).
 from ._lib import (  # noqa: F401
     DOC_ROPE_CHUNK, DOC_ROPE_TOKEN, EXPORTED, LIB_PATH, TOKEN_REDUCE_MAX, TOKEN_REDUCE_MEAN,
     Dims, Interleave, MsaError, dims, encode_pool, lib, plan_chunks, route_topk,
-    route_topk_workspace, sparse_attend, sparse_attend_workspace,
+    route_scores, route_topk_workspace, select_topk, sparse_attend, sparse_attend_workspace,
 )

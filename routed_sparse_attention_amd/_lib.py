@@ -26,6 +26,7 @@ DOC_ROPE_TOKEN, DOC_ROPE_CHUNK = 0, 1
 EXPORTED = [
     "msa_default_dims", "msa_last_error", "msa_abi_version", "msa_plan_chunks",
     "msa_encode_pool_workspace", "msa_encode_pool", "msa_route_topk_workspace", "msa_route_topk",
+    "msa_route_scores_workspace", "msa_route_scores", "msa_select_topk_workspace", "msa_select_topk",
     "msa_sparse_attend_workspace", "msa_sparse_attend", "msa_interleave_reset",
     "msa_interleave_step_workspace", "msa_interleave_step",
 ]
@@ -78,6 +79,11 @@ def lib() -> ctypes.CDLL:
         "msa_route_topk_workspace": (_sz, [_DP, _i32, _i32, _i64, _i32]),
         "msa_route_topk": (_i32, [_DP, _vp, _i32, _i32, _vp, _vp, _i32, _i64, _vp, _i32, _vp, _vp,
                                   _vp, _vp, _sz, _vp]),
+        "msa_route_scores_workspace": (_sz, [_DP, _i32, _i32, _i64]),
+        "msa_route_scores": (_i32, [_DP, _vp, _i32, _i32, _vp, _i64, _vp, _vp, _sz, _vp]),
+        "msa_select_topk_workspace": (_sz, [_DP, _i32, _i32]),
+        "msa_select_topk": (_i32, [_DP, _vp, _i32, _vp, _i32, _i64, _vp, _i32, _vp, _vp, _vp, _vp,
+                                   _sz, _vp]),
         "msa_sparse_attend_workspace": (_sz, [_DP, _i32, _i32, _i64]),
         "msa_sparse_attend": (_i32, [_DP, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i64,
                                      _vp, _i32, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
@@ -197,6 +203,50 @@ def route_topk(QR, KRbar, doc_chunk_offsets, d: Dims | None = None, doc_scores=N
     _check(lib().msa_route_topk(ctypes.byref(d), _p(QR), B, M, _p(KRbar), _p(doc_chunk_offsets),
                                 n_docs, C, _p(doc_scores), int(bool(accumulate)), _p(ids), _p(sc),
                                 _p(ns), _p(ws), ws.numel(), _stream()))
+    return doc_scores, ids, sc, ns
+
+
+def route_scores(QR, KRbar, d: Dims | None = None, out=None, ws=None):
+    """Chunk scores S_c [B, n_chunks] fp32 (first half of route_topk)."""
+    d = d or dims()
+    _need(QR, "QR", torch.bfloat16, ndim=4)
+    _need(KRbar, "KRbar", torch.bfloat16, ndim=3)
+    B, M, C = QR.shape[0], QR.shape[1], KRbar.shape[0]
+    if out is None:
+        out = torch.empty((B, C), dtype=torch.float32, device=QR.device)
+    need = lib().msa_route_scores_workspace(ctypes.byref(d), B, M, C)
+    if need and (ws is None or ws.numel() < need):
+        ws = _workspace(need, QR.device)
+    _check(lib().msa_route_scores(ctypes.byref(d), _p(QR), B, M, _p(KRbar), C, _p(out), _p(ws),
+                                  0 if ws is None else ws.numel(), _stream()))
+    return out
+
+
+def select_topk(chunk_scores, doc_chunk_offsets, d: Dims | None = None, doc_scores=None,
+                accumulate: bool = False, ws=None, outs=None):
+    """Document max + top-k from chunk scores [B, n_chunks] (second half of
+    route_topk): returns (doc_scores, topk_ids, topk_scores, n_sel)."""
+    d = d or dims()
+    _need(chunk_scores, "chunk_scores", torch.float32, ndim=2)
+    _need(doc_chunk_offsets, "doc_chunk_offsets", torch.int64)
+    B, C = chunk_scores.shape
+    n_docs = doc_chunk_offsets.numel() - 1
+    dev = chunk_scores.device
+    if doc_scores is None:
+        if accumulate:
+            raise ValueError("accumulate needs doc_scores")
+        doc_scores = torch.empty((B, n_docs), dtype=torch.float32, device=dev)
+    if outs is None:
+        outs = (torch.empty((B, d.top_k), dtype=torch.int32, device=dev),
+                torch.empty((B, d.top_k), dtype=torch.float32, device=dev),
+                torch.empty((B,), dtype=torch.int32, device=dev))
+    ids, sc, ns = outs
+    need = lib().msa_select_topk_workspace(ctypes.byref(d), B, n_docs)
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, dev)
+    _check(lib().msa_select_topk(ctypes.byref(d), _p(chunk_scores), B, _p(doc_chunk_offsets), n_docs,
+                                 C, _p(doc_scores), int(bool(accumulate)), _p(ids), _p(sc), _p(ns),
+                                 _p(ws), ws.numel(), _stream()))
     return doc_scores, ids, sc, ns
 
 

@@ -78,50 +78,63 @@ int resolve_kv(const void* p, int on_host, const void** out, const char* name) {
   return MSA_OK;
 }
 
-// Routing plan: kernel choice and workspace offsets.
-struct RoutePlan {
+// Scan plan: kernel choice (VALU for <= 8 query rows, MFMA above) and the
+// partials buffer needed when a query's tokens span several row tiles.
+constexpr bool kHaveMfmaScan = false;
+
+struct ScanPlan {
   bool mfma;
   RouteGeom g;
-  int32_t n_slices;
-  size_t off_qh, off_ql, off_S, off_cand, total;
+  size_t parts_bytes;
 };
 
-RoutePlan route_plan(int32_t B, int32_t M, int64_t C, int32_t N, int32_t K) {
-  RoutePlan p;
-  const int64_t rows = (int64_t)B * M;
-  p.mfma = false;
-  p.g = route_geom(B, M, kValuTileRows);
-  (void)rows;
-  p.n_slices = (N + kTopkSlice - 1) / kTopkSlice;
-  size_t o = 0;
-  const size_t qbytes = (size_t)B * M * kRowElems * 2;
-  p.off_qh = o; o = align_up(o + qbytes, 256);
-  p.off_ql = o; o = align_up(o + qbytes, 256);
-  p.off_S = o; o = align_up(o + (size_t)p.g.parts * B * C * 4, 256);
-  p.off_cand = o; o = align_up(o + (size_t)B * p.n_slices * K * 8, 256);
-  p.total = o;
+ScanPlan scan_plan(int32_t B, int32_t M, int64_t C) {
+  ScanPlan p;
+  p.mfma = kHaveMfmaScan && (int64_t)B * M > kValuTileRows;
+  p.g = route_geom(B, M, p.mfma ? kMfmaTileRows : kValuTileRows);
+  p.parts_bytes = p.g.parts > 1 ? align_up((size_t)p.g.parts * B * C * sizeof(float), 256) : 0;
   return p;
+}
+
+int route_scores_impl(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
+                      const msa_bf16* KRbar, int64_t n_chunks, float* S, void* ws, size_t ws_bytes,
+                      hipStream_t s) {
+  const ScanPlan p = scan_plan(B, M, n_chunks);
+  if (p.g.n_tiles > 65535)
+    return fail(MSA_ERR_SHAPE, "route: %d row tiles exceed the grid limit (65535)", p.g.n_tiles);
+  if (ws_bytes < p.parts_bytes || (p.parts_bytes && ws == nullptr))
+    return fail(MSA_ERR_WORKSPACE, "route scores workspace: need %zu bytes, got %zu",
+                p.parts_bytes, ws_bytes);
+  float* dst = p.g.parts > 1 ? static_cast<float*>(ws) : S;
+  int rc = p.mfma ? launch_scan_mfma(QR, p.g, KRbar, n_chunks, d->token_reduce, dst, s)
+                  : launch_scan_valu(QR, p.g, KRbar, n_chunks, d->token_reduce, dst, s);
+  if (rc) return rc;
+  if (p.g.parts > 1) return launch_parts_combine(dst, p.g, n_chunks, d->token_reduce, S, s);
+  return MSA_OK;
+}
+
+size_t route_topk_ws(int32_t B, int32_t M, int64_t C, int32_t N, int32_t K) {
+  const ScanPlan p = scan_plan(B, M, C);
+  const size_t sbytes = align_up((size_t)B * C * sizeof(float), 256);
+  return sbytes + p.parts_bytes + doc_topk_workspace(B, N, K);
 }
 
 int route_topk_impl(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
                     const msa_bf16* KRbar, const int64_t* dco, int32_t n_docs, int64_t n_chunks,
                     float* doc_scores, int32_t accumulate, int32_t* topk_ids, float* topk_scores,
                     int32_t* n_sel, void* ws, size_t ws_bytes, hipStream_t s) {
-  const RoutePlan p = route_plan(B, M, n_chunks, n_docs, d->top_k);
-  if (ws == nullptr || ws_bytes < p.total)
-    return fail(MSA_ERR_WORKSPACE, "route workspace: need %zu bytes, got %zu", p.total, ws_bytes);
+  const size_t need = route_topk_ws(B, M, n_chunks, n_docs, d->top_k);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "route workspace: need %zu bytes, got %zu", need, ws_bytes);
+  const ScanPlan p = scan_plan(B, M, n_chunks);
   char* base = static_cast<char*>(ws);
-  uint16_t* qh = reinterpret_cast<uint16_t*>(base + p.off_qh);
-  uint16_t* ql = reinterpret_cast<uint16_t*>(base + p.off_ql);
-  float* S = reinterpret_cast<float*>(base + p.off_S);
-  uint64_t* cand = reinterpret_cast<uint64_t*>(base + p.off_cand);
-  int rc = launch_qprep(QR, B * M, qh, ql, s);
+  const size_t sbytes = align_up((size_t)B * n_chunks * sizeof(float), 256);
+  float* S = reinterpret_cast<float*>(base);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(base + sbytes + p.parts_bytes);
+  int rc = route_scores_impl(d, QR, B, M, KRbar, n_chunks, S, base + sbytes, p.parts_bytes, s);
   if (rc) return rc;
-  rc = p.mfma ? launch_scan_mfma(qh, ql, p.g, KRbar, n_chunks, d->token_reduce, S, s)
-              : launch_scan_valu(qh, ql, p.g, KRbar, n_chunks, d->token_reduce, S, s);
-  if (rc) return rc;
-  return launch_doc_topk(S, p.g, n_chunks, dco, n_docs, d->token_reduce, doc_scores, accumulate,
-                         d->top_k, cand, topk_ids, topk_scores, n_sel, s);
+  return launch_doc_topk(S, B, n_chunks, dco, n_docs, doc_scores, accumulate, d->top_k, cand,
+                         topk_ids, topk_scores, n_sel, s);
 }
 
 int check_route_args(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
@@ -130,7 +143,8 @@ int check_route_args(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M
                      const float* topk_scores, const int32_t* n_sel) {
   if (!QR || !KRbar || !dco || !doc_scores || !topk_ids || !topk_scores || !n_sel)
     return fail(MSA_ERR_INVALID_ARG, "route: NULL pointer argument");
-  if (B < 1 || M < 1) return fail(MSA_ERR_SHAPE, "route: B=%d M=%d must be >= 1", B, M);
+  if (B < 1 || M < 1 || B > 65535)
+    return fail(MSA_ERR_SHAPE, "route: B=%d M=%d must be >= 1 (B <= 65535)", B, M);
   if ((int64_t)B * M > (1 << 24)) return fail(MSA_ERR_SHAPE, "route: B*M too large");
   if (n_docs < 1) return fail(MSA_ERR_SHAPE, "route: n_docs=%d must be >= 1", n_docs);
   if (n_chunks < n_docs || n_chunks >= ((int64_t)1 << 31))
@@ -236,10 +250,57 @@ int32_t msa_encode_pool(const msa_dims* d, const msa_bf16* K, const msa_bf16* V,
   return launch_pool(a, static_cast<hipStream_t>(stream));
 }
 
+size_t msa_route_scores_workspace(const msa_dims* d, int32_t B, int32_t M, int64_t n_chunks) {
+  if (!d || B < 1 || M < 1 || n_chunks < 1) return 0;
+  return scan_plan(B, M, n_chunks).parts_bytes;
+}
+
+int32_t msa_route_scores(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
+                         const msa_bf16* KRbar, int64_t n_chunks, float* chunk_scores, void* ws,
+                         size_t ws_bytes, void* stream) {
+  clear_error();
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!QR || !KRbar || !chunk_scores) return fail(MSA_ERR_INVALID_ARG, "route_scores: NULL pointer");
+  if (B < 1 || M < 1) return fail(MSA_ERR_SHAPE, "route_scores: B=%d M=%d must be >= 1", B, M);
+  if ((int64_t)B * M > (1 << 24)) return fail(MSA_ERR_SHAPE, "route_scores: B*M too large");
+  if (n_chunks < 1 || n_chunks >= ((int64_t)1 << 31))
+    return fail(MSA_ERR_SHAPE, "route_scores: n_chunks=%lld out of [1, 2^31)", (long long)n_chunks);
+  return route_scores_impl(d, QR, B, M, KRbar, n_chunks, chunk_scores, ws, ws_bytes,
+                           static_cast<hipStream_t>(stream));
+}
+
+size_t msa_select_topk_workspace(const msa_dims* d, int32_t B, int32_t n_docs) {
+  if (!d || B < 1 || n_docs < 1 || d->top_k < 1) return 0;
+  return doc_topk_workspace(B, n_docs, d->top_k);
+}
+
+int32_t msa_select_topk(const msa_dims* d, const float* chunk_scores, int32_t B, const int64_t* dco,
+                        int32_t n_docs, int64_t n_chunks, float* doc_scores, int32_t accumulate,
+                        int32_t* topk_ids, float* topk_scores, int32_t* n_sel, void* ws,
+                        size_t ws_bytes, void* stream) {
+  clear_error();
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!chunk_scores || !dco || !doc_scores || !topk_ids || !topk_scores || !n_sel)
+    return fail(MSA_ERR_INVALID_ARG, "select_topk: NULL pointer argument");
+  if (B < 1 || B > 65535) return fail(MSA_ERR_SHAPE, "select_topk: B=%d out of [1, 65535]", B);
+  if (n_docs < 1) return fail(MSA_ERR_SHAPE, "select_topk: n_docs=%d must be >= 1", n_docs);
+  if (n_chunks < n_docs || n_chunks >= ((int64_t)1 << 31))
+    return fail(MSA_ERR_SHAPE, "select_topk: n_chunks=%lld must be in [n_docs, 2^31)",
+                (long long)n_chunks);
+  const size_t need = doc_topk_workspace(B, n_docs, d->top_k);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "select_topk workspace: need %zu bytes, got %zu", need, ws_bytes);
+  return launch_doc_topk(chunk_scores, B, n_chunks, dco, n_docs, doc_scores, accumulate, d->top_k,
+                         static_cast<uint64_t*>(ws), topk_ids, topk_scores, n_sel,
+                         static_cast<hipStream_t>(stream));
+}
+
 size_t msa_route_topk_workspace(const msa_dims* d, int32_t B, int32_t M, int64_t n_chunks,
                                 int32_t n_docs) {
   if (!d || B < 1 || M < 1 || n_chunks < 1 || n_docs < 1) return 0;
-  return route_plan(B, M, n_chunks, n_docs, d->top_k).total;
+  return route_topk_ws(B, M, n_chunks, n_docs, d->top_k);
 }
 
 int32_t msa_route_topk(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
@@ -311,7 +372,7 @@ size_t msa_interleave_step_workspace(const msa_dims* d, int32_t M_new, int32_t c
                                      int64_t n_chunks, int32_t n_docs, int64_t max_sel_chunks) {
   if (!d || M_new < 1 || cap_loc < M_new || n_chunks < 1 || n_docs < 1 || max_sel_chunks < 0)
     return 0;
-  const size_t r = route_plan(1, M_new, n_chunks, n_docs, d->top_k).total;
+  const size_t r = route_topk_ws(1, M_new, n_chunks, n_docs, d->top_k);
   const size_t a = attend_workspace(M_new, cap_loc, d->n_q_heads, max_sel_chunks);
   return r > a ? r : a;
 }
@@ -340,7 +401,7 @@ int32_t msa_interleave_step(const msa_dims* d, msa_interleave_state* st, const m
   rc = check_attend_args(d, Q_new, M_new, st->K_loc, st->V_loc, M_loc, Kbar, Vbar, n_chunks, dco,
                          n_docs, st->topk_ids, st->n_sel, max_sel_chunks, out);
   if (rc) return rc;
-  const size_t need_r = route_plan(1, M_new, n_chunks, n_docs, d->top_k).total;
+  const size_t need_r = route_topk_ws(1, M_new, n_chunks, n_docs, d->top_k);
   const size_t need_a = attend_workspace(M_new, M_loc, d->n_q_heads, max_sel_chunks);
   if (ws == nullptr || ws_bytes < need_r || ws_bytes < need_a)
     return fail(MSA_ERR_WORKSPACE, "interleave workspace too small");

@@ -78,6 +78,40 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// q̂ = x / max(‖x‖, eps) (fp64) for the 16 dims [16(l%8), +16) of head l/8
+// held by this lane (the head's other dims sit in the 7 neighbouring lanes of
+// the same group of 8), returned as bf16 hi + lo vectors of 8 dims each.
+__device__ inline void qhat_hilo16(const uint16_t* row, int lane, uint4* hi, uint4* lo) {
+  const uint4* src = reinterpret_cast<const uint4*>(row) + 2 * lane;
+  const uint4 a = src[0], b = src[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  double x[16];
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = bf16lo(w[i]);
+    x[2 * i + 1] = bf16hi(w[i]);
+    ss += x[2 * i] * x[2 * i] + x[2 * i + 1] * x[2 * i + 1];
+  }
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+  ss += __shfl_xor(ss, 4);
+  const double nrm = sqrt(ss);
+  const double inv = 1.0 / (nrm > (double)kNormEps ? nrm : (double)kNormEps);
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double q0 = x[2 * i] * inv, q1 = x[2 * i + 1] * inv;
+    const uint16_t h0 = d2bf(q0), h1 = d2bf(q1);
+    h[i] = pack2(h0, h1);
+    l[i] = pack2(d2bf(q0 - (double)bf16f(h0)), d2bf(q1 - (double)bf16f(h1)));
+  }
+  hi[0] = make_uint4(h[0], h[1], h[2], h[3]);
+  hi[1] = make_uint4(h[4], h[5], h[6], h[7]);
+  lo[0] = make_uint4(l[0], l[1], l[2], l[3]);
+  lo[1] = make_uint4(l[4], l[5], l[6], l[7]);
+}
+
 // Order-preserving map of a float onto uint32 (larger float -> larger key).
 // NaN maps to 0 (ranks below every number); -0 is treated as +0.
 __device__ __forceinline__ uint32_t ord_key(float f) {
@@ -110,8 +144,8 @@ struct PoolArgs {
 };
 int launch_pool(const PoolArgs& a, hipStream_t s);
 
-// Router-query preparation + chunk scan. The chunk scores are reduced over
-// the query tokens inside one row tile; S holds [parts][B][C] fp32.
+// Routing scan geometry. Query rows are processed in tiles of `tile_rows`:
+// whole queries per tile when M <= tile_rows, else `parts` tiles per query.
 struct RouteGeom {
   int32_t B, M;           // queries, tokens per query
   int32_t tile_rows;      // rows per tile (kernel dependent)
@@ -120,21 +154,48 @@ struct RouteGeom {
   int32_t n_tiles;        // row tiles in the grid
 };
 RouteGeom route_geom(int32_t B, int32_t M, int32_t tile_rows);
-int launch_qprep(const uint16_t* QR, int32_t rows, uint16_t* q_hi, uint16_t* q_lo, hipStream_t s);
-int launch_scan_valu(const uint16_t* q_hi, const uint16_t* q_lo, const RouteGeom& g,
-                     const uint16_t* KRbar, int64_t n_chunks, int32_t token_reduce,
-                     float* S, hipStream_t s);
-int launch_scan_mfma(const uint16_t* q_hi, const uint16_t* q_lo, const RouteGeom& g,
-                     const uint16_t* KRbar, int64_t n_chunks, int32_t token_reduce,
-                     float* S, hipStream_t s);
+
+// Rows of tile `ty`: queries [b0, b0+nq), tokens [m0, m0+nr) of each.
+struct TileRows {
+  int32_t b0, nq;
+  int32_t part;
+  int32_t m0, nr;
+};
+__host__ __device__ inline TileRows tile_rows_of(const RouteGeom& g, int ty) {
+  TileRows t;
+  if (g.parts == 1) {
+    t.b0 = ty * g.q_per_tile;
+    t.nq = g.B - t.b0 < g.q_per_tile ? g.B - t.b0 : g.q_per_tile;
+    t.part = 0;
+    t.m0 = 0;
+    t.nr = g.M;
+  } else {
+    t.b0 = ty / g.parts;
+    t.nq = 1;
+    t.part = ty % g.parts;
+    t.m0 = t.part * g.tile_rows;
+    t.nr = g.M - t.m0 < g.tile_rows ? g.M - t.m0 : g.tile_rows;
+  }
+  return t;
+}
+
+// Scan output: with parts == 1 the kernels write final chunk scores S[B][C]
+// (MEAN already divided by M); with parts > 1 they write per-part partials
+// P[parts][B][C] (max, or sums under MEAN) that launch_parts_combine folds.
 constexpr int kValuTileRows = 8;
 constexpr int kMfmaTileRows = 64;
+int launch_scan_valu(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRbar,
+                     int64_t n_chunks, int32_t token_reduce, float* out, hipStream_t s);
+int launch_scan_mfma(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRbar,
+                     int64_t n_chunks, int32_t token_reduce, float* out, hipStream_t s);
+int launch_parts_combine(const float* P, const RouteGeom& g, int64_t n_chunks,
+                         int32_t token_reduce, float* S, hipStream_t s);
 
 // Doc reduce + top-k.
 constexpr int kTopkSlice = 1024;   // documents per stage-1 workgroup
-int launch_doc_topk(const float* S, const RouteGeom& g, int64_t n_chunks,
-                    const int64_t* dco, int32_t n_docs, int32_t token_reduce,
-                    float* doc_scores, int32_t accumulate, int32_t top_k,
+size_t doc_topk_workspace(int32_t B, int32_t n_docs, int32_t top_k);
+int launch_doc_topk(const float* S, int32_t B, int64_t n_chunks, const int64_t* dco,
+                    int32_t n_docs, float* doc_scores, int32_t accumulate, int32_t top_k,
                     uint64_t* cand, int32_t* topk_ids, float* topk_scores, int32_t* n_sel,
                     hipStream_t s);
 int launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);

@@ -7,19 +7,20 @@
 //
 // Design. The store is read once per row tile and never written; the
 // [tokens × chunks] score matrix is never materialised — tokens are reduced
-// inside a tile, so only S[parts][B][C] (4 bytes per chunk per query part)
-// leaves the kernel. Under the MEAN reduction a tile stores the sum of its
-// rows; the document stage divides by M.
-//   qprep: q̂ = Q^R / max(‖Q^R‖, eps) per head, split into bf16 hi + lo parts
-//     (q̂ ≈ hi + lo to ~2^-17), so bf16 dot products against the bf16 keys
-//     keep fp32-level accuracy.
+// inside a tile, so only 4 bytes per chunk per query leave the kernel. When a
+// query's tokens span several tiles (M > tile rows) each tile writes a
+// partial (max, or sum under MEAN) and parts_combine_kernel folds them.
+//   Router queries are normalised inside the scan kernels: q̂ = Q^R /
+//     max(‖Q^R‖, eps) per head in fp64, split into bf16 hi + lo parts
+//     (q̂ ≈ hi + lo to ~2^-17), so bf16 products against the bf16 keys keep
+//     fp32-level accuracy.
 //   scan_valu (decode and small batches, <= 8 rows per tile): HBM-bound
 //     stream. Lane l of a wave owns head l/8, dims [16(l%8), 16(l%8)+16) of
 //     one chunk; it keeps its slice of every tile row's q̂ in registers for
 //     the whole launch. Per chunk: two 16-byte loads, v_dot2 bf16 products for
 //     q̂·k (hi and lo) and k·k, an 8-lane reduction per head, a per-head
 //     1/max(‖k‖, eps) scale and an 8-group reduction over heads.
-//   scan_mfma (batched rows): see msa_route_mfma.hip.
+//   scan_mfma (batched rows): msa_route_mfma.hip.
 #include "msa_internal.h"
 
 namespace msa {
@@ -50,93 +51,31 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// One wave per router-query row: lane l owns head l/8, dims 16(l%8)..+16.
-__global__ __launch_bounds__(256) void qprep_kernel(const uint16_t* __restrict__ QR, int32_t rows,
-                                                    uint16_t* __restrict__ q_hi,
-                                                    uint16_t* __restrict__ q_lo) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const uint16_t* src = QR + r * kRowElems + lane * 16;
-  float x[16];
-  double ss = 0.0;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    x[e] = bf16f(src[e]);
-    ss += (double)x[e] * (double)x[e];
-  }
-  // sum over the 8 lanes of this head
-  ss += __shfl_xor(ss, 1);
-  ss += __shfl_xor(ss, 2);
-  ss += __shfl_xor(ss, 4);
-  const double nrm = sqrt(ss);
-  const double inv = 1.0 / (nrm > (double)kNormEps ? nrm : (double)kNormEps);
-  uint16_t* dh = q_hi + r * kRowElems + lane * 16;
-  uint16_t* dl = q_lo + r * kRowElems + lane * 16;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const double q = (double)x[e] * inv;
-    const uint16_t hb = d2bf(q);
-    dh[e] = hb;
-    dl[e] = d2bf(q - (double)bf16f(hb));
-  }
-}
-
-// Rows of tile `ty`: for M <= tile_rows, whole queries [b0, b0+nq) with M rows
-// each; otherwise rows [m0, m0+nr) of query b. Row index r -> (query, token).
-struct TileRows {
-  int32_t b0, nq;      // first query and query count in this tile
-  int32_t part;        // part index (0 when whole queries)
-  int32_t m0, nr;      // token range of each query covered by this tile
-};
-
-__device__ __forceinline__ TileRows tile_rows_of(const RouteGeom& g, int ty) {
-  TileRows t;
-  if (g.parts == 1) {
-    t.b0 = ty * g.q_per_tile;
-    t.nq = min(g.q_per_tile, g.B - t.b0);
-    t.part = 0;
-    t.m0 = 0;
-    t.nr = g.M;
-  } else {
-    t.b0 = ty / g.parts;
-    t.nq = 1;
-    t.part = ty % g.parts;
-    t.m0 = t.part * g.tile_rows;
-    t.nr = min(g.tile_rows, g.M - t.m0);
-  }
-  return t;
-}
-
 constexpr int kScanWaves = 4;
 constexpr int kScanUnroll = 4;
 
 template <int R>
-__global__ __launch_bounds__(256) void scan_valu_kernel(const uint4* __restrict__ q_hi,
-                                                        const uint4* __restrict__ q_lo,
+__global__ __launch_bounds__(256) void scan_valu_kernel(const uint16_t* __restrict__ QR,
                                                         RouteGeom g, const uint4* __restrict__ KR,
                                                         int64_t n_chunks, int32_t token_reduce,
-                                                        float* __restrict__ S) {
+                                                        float* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const TileRows tr = tile_rows_of(g, blockIdx.y);
   const int n_rows = tr.nq * tr.nr;  // <= R
-  // this lane's slice of every row's q̂ (two 16-byte vectors, hi and lo)
+  // this lane's slice of every tile row's q̂ (hi and lo, two 16-byte vectors each)
   uint4 qh[R][2], ql[R][2];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     if (k < n_rows) {
-      const int qb = tr.b0 + k / tr.nr;
-      const int m = tr.m0 + k % tr.nr;
-      const int64_t row = (int64_t)qb * g.M + m;
-      qh[k][0] = q_hi[row * kRowVec + 2 * lane];
-      qh[k][1] = q_hi[row * kRowVec + 2 * lane + 1];
-      ql[k][0] = q_lo[row * kRowVec + 2 * lane];
-      ql[k][1] = q_lo[row * kRowVec + 2 * lane + 1];
+      const int64_t row = (int64_t)(tr.b0 + k / tr.nr) * g.M + tr.m0 + k % tr.nr;
+      qhat_hilo16(QR + row * kRowElems, lane, qh[k], ql[k]);
     } else {
       qh[k][0] = qh[k][1] = ql[k][0] = ql[k][1] = make_uint4(0, 0, 0, 0);
     }
   }
+  const bool mean = token_reduce == MSA_TOKEN_REDUCE_MEAN;
+  const float fin = (mean && g.parts == 1) ? 1.0f / (float)g.M : 1.0f;
   const int64_t wave_id = (int64_t)blockIdx.x * kScanWaves + wave;
   const int64_t n_waves = (int64_t)gridDim.x * kScanWaves;
 
@@ -165,7 +104,7 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const uint4* __restrict_
       nrm += __shfl_xor(nrm, 4);
       const float kn = sqrtf(nrm);
       const float inv_k = 1.0f / (kn > kNormEps ? kn : kNormEps);
-      float red[R > 0 ? R : 1];
+      float red[R];
 #pragma unroll
       for (int k = 0; k < R; ++k) {
         const uint32_t hw[8] = {qh[k][0].x, qh[k][0].y, qh[k][0].z, qh[k][0].w,
@@ -193,51 +132,67 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const uint4* __restrict_
         if (k < n_rows) {
           const int m = k % tr.nr;
           const float x = red[k];
-          v = (m == 0) ? x : (token_reduce == MSA_TOKEN_REDUCE_MAX ? nan_max(v, x) : v + x);
+          v = (m == 0) ? x : (mean ? v + x : nan_max(v, x));
           if (m == tr.nr - 1 && lane == 0 && c < n_chunks)
-            S[((int64_t)tr.part * g.B + tr.b0 + k / tr.nr) * n_chunks + c] = v;
+            out[((int64_t)tr.part * g.B + tr.b0 + k / tr.nr) * n_chunks + c] = v * fin;
         }
       }
     }
   }
 }
 
+// S[b][c] = fold over parts of P[part][b][c] (max, or sum / M under MEAN).
+__global__ __launch_bounds__(256) void parts_combine_kernel(const float* __restrict__ P,
+                                                            RouteGeom g, int64_t C,
+                                                            int32_t token_reduce,
+                                                            float* __restrict__ S) {
+  const int64_t n = (int64_t)g.B * C;
+  const bool mean = token_reduce == MSA_TOKEN_REDUCE_MEAN;
+  const float inv_m = 1.0f / (float)g.M;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float v = P[i];
+    for (int p = 1; p < g.parts; ++p) {
+      const float x = P[(int64_t)p * n + i];
+      v = mean ? v + x : nan_max(v, x);
+    }
+    S[i] = mean ? v * inv_m : v;
+  }
+}
+
 }  // namespace
 
-int launch_qprep(const uint16_t* QR, int32_t rows, uint16_t* q_hi, uint16_t* q_lo, hipStream_t s) {
-  if (rows == 0) return MSA_OK;
-  hipLaunchKernelGGL(qprep_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, QR, rows, q_hi, q_lo);
-  MSA_LAUNCH_CHECK("qprep_kernel launch");
+int launch_scan_valu(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRbar,
+                     int64_t n_chunks, int32_t token_reduce, float* out, hipStream_t s) {
+  if (n_chunks == 0 || g.n_tiles == 0) return MSA_OK;
+  // at most 2048 workgroups (8 per CU); each wave strides over the store
+  const int64_t per_wg = (int64_t)kScanWaves * kScanUnroll;
+  int64_t wg = (n_chunks + per_wg - 1) / per_wg;
+  if (wg > 2048) wg = 2048;
+  const dim3 grid((unsigned)wg, (unsigned)g.n_tiles);
+  const uint4* kr = reinterpret_cast<const uint4*>(KRbar);
+  const int rows = g.parts == 1 ? g.q_per_tile * g.M : g.tile_rows;
+  if (rows <= 1)
+    hipLaunchKernelGGL(scan_valu_kernel<1>, grid, dim3(256), 0, s, QR, g, kr, n_chunks, token_reduce, out);
+  else if (rows <= 2)
+    hipLaunchKernelGGL(scan_valu_kernel<2>, grid, dim3(256), 0, s, QR, g, kr, n_chunks, token_reduce, out);
+  else if (rows <= 4)
+    hipLaunchKernelGGL(scan_valu_kernel<4>, grid, dim3(256), 0, s, QR, g, kr, n_chunks, token_reduce, out);
+  else
+    hipLaunchKernelGGL(scan_valu_kernel<8>, grid, dim3(256), 0, s, QR, g, kr, n_chunks, token_reduce, out);
+  MSA_LAUNCH_CHECK("scan_valu_kernel launch");
   return MSA_OK;
 }
 
-int launch_scan_valu(const uint16_t* q_hi, const uint16_t* q_lo, const RouteGeom& g,
-                     const uint16_t* KRbar, int64_t n_chunks, int32_t token_reduce, float* S,
-                     hipStream_t s) {
-  if (n_chunks == 0 || g.n_tiles == 0) return MSA_OK;
-  // enough waves to keep every CU streaming: 256 CUs × 8 workgroups
-  int64_t per_wg = (int64_t)kScanWaves * kScanUnroll;
-  int64_t wg = (n_chunks + per_wg - 1) / per_wg;
-  if (wg > 2048) wg = 2048;
-  dim3 grid((unsigned)wg, (unsigned)g.n_tiles);
-  const uint4* qh = reinterpret_cast<const uint4*>(q_hi);
-  const uint4* ql = reinterpret_cast<const uint4*>(q_lo);
-  const uint4* kr = reinterpret_cast<const uint4*>(KRbar);
-  const int rows = g.parts == 1 ? g.q_per_tile * g.M : g.tile_rows;
-  if (rows <= 1) {
-    hipLaunchKernelGGL(scan_valu_kernel<1>, grid, dim3(256), 0, s, qh, ql, g, kr, n_chunks,
-                       token_reduce, S);
-  } else if (rows <= 2) {
-    hipLaunchKernelGGL(scan_valu_kernel<2>, grid, dim3(256), 0, s, qh, ql, g, kr, n_chunks,
-                       token_reduce, S);
-  } else if (rows <= 4) {
-    hipLaunchKernelGGL(scan_valu_kernel<4>, grid, dim3(256), 0, s, qh, ql, g, kr, n_chunks,
-                       token_reduce, S);
-  } else {
-    hipLaunchKernelGGL(scan_valu_kernel<8>, grid, dim3(256), 0, s, qh, ql, g, kr, n_chunks,
-                       token_reduce, S);
-  }
-  MSA_LAUNCH_CHECK("scan_valu_kernel launch");
+int launch_parts_combine(const float* P, const RouteGeom& g, int64_t n_chunks,
+                         int32_t token_reduce, float* S, hipStream_t s) {
+  const int64_t n = (int64_t)g.B * n_chunks;
+  if (n == 0) return MSA_OK;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(parts_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, P, g, n_chunks,
+                     token_reduce, S);
+  MSA_LAUNCH_CHECK("parts_combine_kernel launch");
   return MSA_OK;
 }
 

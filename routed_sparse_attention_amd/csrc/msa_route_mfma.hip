@@ -3,8 +3,8 @@
 
 namespace msa {
 
-int launch_scan_mfma(const uint16_t*, const uint16_t*, const RouteGeom&, const uint16_t*, int64_t,
-                     int32_t, float*, hipStream_t) {
+int launch_scan_mfma(const uint16_t*, const RouteGeom&, const uint16_t*, int64_t, int32_t, float*,
+                     hipStream_t) {
   return fail(MSA_ERR_UNSUPPORTED, "MFMA routing scan not built");
 }
 

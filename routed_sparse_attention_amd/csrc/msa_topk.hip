@@ -4,8 +4,7 @@
 // Method (portal.techblg.uk IRMaD reading, section M, routing bullet):
 //   s_i = max_j S_ij over document i's chunks, I = Top-k({s_i}), k = 16.
 // Readings: ties go to the lowest document id; with fewer than k documents
-// all are selected; a NaN score ranks below every number; under the MEAN
-// token reduction S is the token sum over all parts divided by M.
+// all are selected; a NaN score ranks below every number.
 //
 // Design. Every document score becomes one unique 64-bit key
 //   (order-preserving uint32 of the score) << 32 | (0xFFFFFFFF − id),
@@ -51,9 +50,9 @@ __device__ __forceinline__ uint64_t doc_key(float s, int32_t i) {
   return ((uint64_t)ord_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
 }
 
-__global__ __launch_bounds__(256) void doc_topk1_kernel(const float* __restrict__ S, RouteGeom g,
-                                                        int64_t C, const int64_t* __restrict__ dco,
-                                                        int32_t n_docs, int32_t token_reduce,
+__global__ __launch_bounds__(256) void doc_topk1_kernel(const float* __restrict__ S, int64_t C,
+                                                        const int64_t* __restrict__ dco,
+                                                        int32_t n_docs,
                                                         float* __restrict__ doc_scores,
                                                         int32_t accumulate, int32_t K,
                                                         uint64_t* __restrict__ cand,
@@ -62,7 +61,6 @@ __global__ __launch_bounds__(256) void doc_topk1_kernel(const float* __restrict_
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
   const int slice = blockIdx.x;
-  const float inv_m = 1.0f / (float)g.M;
   for (int q = 0; q < kSortN / kThreads; ++q) {
     const int64_t i = (int64_t)slice * kSortN + q * kThreads + tid;
     uint64_t key = 0;
@@ -71,15 +69,8 @@ __global__ __launch_bounds__(256) void doc_topk1_kernel(const float* __restrict_
       c0 = max((int64_t)0, min(c0, C));
       c1 = max(c0, min(c1, C));
       float s = -INFINITY;
-      for (int64_t c = c0; c < c1; ++c) {
-        float v = S[(int64_t)b * C + c];
-        for (int part = 1; part < g.parts; ++part) {
-          const float x = S[((int64_t)part * g.B + b) * C + c];
-          v = token_reduce == MSA_TOKEN_REDUCE_MAX ? nan_max(v, x) : v + x;
-        }
-        if (token_reduce == MSA_TOKEN_REDUCE_MEAN) v *= inv_m;
-        s = (c == c0) ? v : nan_max(s, v);
-      }
+      const float* Sb = S + (int64_t)b * C;
+      for (int64_t c = c0; c < c1; ++c) s = (c == c0) ? Sb[c] : nan_max(s, Sb[c]);
       float* ds = doc_scores + (int64_t)b * n_docs + i;
       if (accumulate) s = nan_max(*ds, s);
       *ds = s;
@@ -136,15 +127,20 @@ __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
 
 }  // namespace
 
-int launch_doc_topk(const float* S, const RouteGeom& g, int64_t n_chunks, const int64_t* dco,
-                    int32_t n_docs, int32_t token_reduce, float* doc_scores, int32_t accumulate,
-                    int32_t top_k, uint64_t* cand, int32_t* topk_ids, float* topk_scores,
-                    int32_t* n_sel, hipStream_t s) {
+size_t doc_topk_workspace(int32_t B, int32_t n_docs, int32_t top_k) {
+  const int64_t n_slices = (n_docs + kSortN - 1) / kSortN;
+  return align_up((size_t)B * n_slices * top_k * sizeof(uint64_t), 256);
+}
+
+int launch_doc_topk(const float* S, int32_t B, int64_t n_chunks, const int64_t* dco,
+                    int32_t n_docs, float* doc_scores, int32_t accumulate, int32_t top_k,
+                    uint64_t* cand, int32_t* topk_ids, float* topk_scores, int32_t* n_sel,
+                    hipStream_t s) {
   const int32_t n_slices = (n_docs + kSortN - 1) / kSortN;
-  hipLaunchKernelGGL(doc_topk1_kernel, dim3(n_slices, g.B), dim3(kThreads), 0, s, S, g, n_chunks,
-                     dco, n_docs, token_reduce, doc_scores, accumulate, top_k, cand, n_slices);
+  hipLaunchKernelGGL(doc_topk1_kernel, dim3(n_slices, B), dim3(kThreads), 0, s, S, n_chunks, dco,
+                     n_docs, doc_scores, accumulate, top_k, cand, n_slices);
   MSA_LAUNCH_CHECK("doc_topk1_kernel launch");
-  hipLaunchKernelGGL(doc_topk2_kernel, dim3(g.B), dim3(kThreads), 0, s, cand, n_slices, top_k,
+  hipLaunchKernelGGL(doc_topk2_kernel, dim3(B), dim3(kThreads), 0, s, cand, n_slices, top_k,
                      n_docs, topk_ids, topk_scores, n_sel);
   MSA_LAUNCH_CHECK("doc_topk2_kernel launch");
   return MSA_OK;

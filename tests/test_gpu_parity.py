@@ -318,3 +318,37 @@ def test_workspace_too_small():
     torch.cuda.synchronize()
     assert rc == -3 and b"workspace" in lib.msa_last_error()
     assert torch.all(ds == 7.0) and torch.all(ids == 5)   # nothing written on error
+
+
+# ---------------------------------------------------------------------------
+# the two halves of routing as separate calls
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,M", [(1, 1), (2, 40)])
+def test_route_scores_call(B, M):
+    _banner(f"route_scores B={B} M={M}")
+    st = _store(1500, 91 + M)
+    QR = synth.randn_bf16((B, M, 8, 128), synth.torch_gen(10, M))
+    S = msa.route_scores(QR.to(DEV), st.KRbar.to(DEV))
+    torch.cuda.synchronize()
+    for b in range(B):
+        assert_scores_close(S[b].cpu().numpy(), O.chunk_scores(u16(QR[b]), u16(st.KRbar)),
+                            f"chunk scores q{b}")
+
+
+def test_select_topk_exact_on_given_scores():
+    _banner("select_topk on synthetic chunk scores")
+    rng = synth.np_rng(92, 0)
+    counts = synth.counts_until(rng, 40_000, 1, 64)
+    dco_h = synth.offsets_from_lengths(counts)
+    C = int(dco_h[-1])
+    # fp32 chunk scores with repeated values (ties) drawn by the generator
+    S = (rng.integers(-300, 300, size=(3, C)) / 300.0).astype(np.float32)
+    d = msa.dims()
+    ds, ids, sc, ns = msa.select_topk(torch.from_numpy(S).to(DEV), torch.from_numpy(dco_h).to(DEV), d)
+    torch.cuda.synchronize()
+    for b in range(3):
+        s = O.doc_scores(S[b].astype(np.float64), dco_h)
+        assert np.array_equal(ds[b].cpu().numpy().astype(np.float64), s)
+        exp_ids, exp_sc, _ = O.topk(s, 16)
+        assert list(ids[b].cpu().numpy()) == list(exp_ids)      # bit-exact, ties included
+        assert int(ns[b]) == 16
