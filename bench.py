@@ -199,7 +199,7 @@ def main():
         msa.route_scores(QR[l], store.KRbar[l], d, out=S)
         msa.select_topk(S, dco, d, doc_scores=ds, ws=ws_sel, outs=(ids, sc, ns))
         got = set(ids[0].cpu().tolist())
-        assert set(queries[l].planted[0]) <= got, f"layer {l}: needle not selected"
+        assert set(queries[l].planted_docs[0]) <= got, f"layer {l}: needle not selected"
     log(args, "needles found in every layer")
 
     for _ in range(args.warmup):

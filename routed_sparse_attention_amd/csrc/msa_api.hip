@@ -290,7 +290,7 @@ int32_t msa_select_topk(const msa_dims* d, const float* chunk_scores, int32_t B,
     return fail(MSA_ERR_SHAPE, "select_topk: n_chunks=%lld must be in [n_docs, 2^31)",
                 (long long)n_chunks);
   const size_t need = doc_topk_workspace(B, n_docs, d->top_k);
-  if (ws == nullptr || ws_bytes < need)
+  if (need && (ws == nullptr || ws_bytes < need))
     return fail(MSA_ERR_WORKSPACE, "select_topk workspace: need %zu bytes, got %zu", need, ws_bytes);
   return launch_doc_topk(chunk_scores, B, n_chunks, dco, n_docs, doc_scores, accumulate, d->top_k,
                          static_cast<uint64_t*>(ws), topk_ids, topk_scores, n_sel,

@@ -12,21 +12,22 @@
 // and local keys causal; logits scale 1/sqrt(128); q head h reads KV head
 // h / (Hq / 8); memory chunks enter in rank order.
 //
-// Pipeline (one stream, four launches):
-//   assemble  (1 wave)   selected ids -> list of memory chunk rows, n_mem,
-//                        resolved pos0;
-//   rope      (elementwise) Q and K_loc rotated once into the workspace (bf16);
-//   attn      (MFMA)     flash attention, one wave per (32 query rows of one KV
-//                        group, KV head, key split): S = Q·K^T with
-//                        v_mfma_f32_32x32x16_bf16 (K fragments loaded straight
-//                        from memory — 16 contiguous bytes per lane), online
-//                        softmax in fp32 (exp2 domain), P re-laid out through
-//                        LDS, V staged transposed in LDS so its MFMA fragments
-//                        are 16-byte LDS reads, O += P·V. Memory rows are read
-//                        in place, from HBM or from pinned host memory over
-//                        PCIe (no staging copy);
-//   combine              merges the key splits (log-sum-exp) and writes bf16
-//                        (and optionally fp32) output.
+// Pipeline (one stream, three launches):
+//   prep      block 0 turns the selected ids into the list of memory chunk
+//             rows (and n_mem); the other blocks rotate Q and K_loc into the
+//             workspace (bf16), one thread per rotation pair;
+//   attn      flash attention, one wave per (32 query rows of one KV group,
+//             KV head, key split). Each 32-key tile of K and V is read with
+//             one 256-byte row per 16 lanes (coalesced, and large PCIe reads
+//             when K̄/V̄ sit in pinned host memory — they are read in place,
+//             with no staging copy) and staged in LDS: K row-major, V
+//             transposed, so both MFMA B fragments are 16-byte LDS reads.
+//             S = Q·K^T and O += P·V use v_mfma_f32_32x32x16_bf16; the online
+//             softmax runs in fp32 in the exp2 domain; P is re-laid out from
+//             the accumulator layout to the A-operand layout through LDS;
+//   combine   merges the key splits (log-sum-exp weights computed once per
+//             row in LDS, then one independent load per split and dim) and
+//             writes bf16 (and optionally fp32) output.
 #include "msa_internal.h"
 
 namespace msa {
@@ -37,103 +38,100 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kKeyTile = 32;
 constexpr int kRowTile = 32;
+constexpr int kMaxSplits = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnWs {
   int32_t* mem_rows;   // [max_sel_chunks]
   int32_t* n_mem;      // [1]
-  int64_t* pos0;       // [1]
   uint16_t* Qr;        // [M][Hq][128]
   uint16_t* Kr;        // [M_loc][8][128]
   float* Opart;        // [n_splits][M*Hq][128]
   float* ML;           // [n_splits][M*Hq][2]
 };
 
-__global__ __launch_bounds__(64) void assemble_kernel(const int32_t* __restrict__ sel_ids,
-                                                      const int32_t* __restrict__ n_sel_p,
-                                                      int32_t top_k,
-                                                      const int64_t* __restrict__ dco,
-                                                      int32_t n_docs, int64_t n_chunks,
-                                                      int64_t max_sel, int64_t pos0_in,
-                                                      int32_t* __restrict__ mem_rows,
-                                                      int32_t* __restrict__ n_mem,
-                                                      int64_t* __restrict__ pos0_out) {
-  const int lane = threadIdx.x;
-  int ns = *n_sel_p;
-  ns = ns < 0 ? 0 : (ns > top_k ? top_k : ns);
-  int64_t start = 0, cnt = 0;
-  if (lane < ns) {
-    const int32_t id = sel_ids[lane];
-    if (id >= 0 && id < n_docs) {
-      int64_t c0 = dco[id], c1 = dco[id + 1];
-      c0 = max((int64_t)0, min(c0, n_chunks));
-      c1 = max(c0, min(c1, n_chunks));
-      start = c0;
-      cnt = c1 - c0;
-    }
-  }
-  // exclusive prefix sum of cnt over the wave
-  int64_t incl = cnt;
-  for (int d = 1; d < 64; d <<= 1) {
-    const int64_t y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
-  }
-  const int64_t off = incl - cnt;
-  const int64_t total = __shfl(incl, 63);
-  for (int64_t j = 0; j < cnt && off + j < max_sel; ++j) mem_rows[off + j] = (int32_t)(start + j);
-  if (lane == 0) {
-    *n_mem = (int32_t)(total < max_sel ? total : max_sel);
-    *pos0_out = pos0_in < 0 ? (int64_t)ns : pos0_in;
-  }
+struct PrepArgs {
+  const int32_t* sel_ids; const int32_t* n_sel; int32_t top_k;
+  const int64_t* dco; int32_t n_docs; int64_t n_chunks; int64_t max_sel; int64_t pos0;
+  const uint16_t* Q; int32_t M; int32_t Hq;
+  const uint16_t* Kl; int32_t M_loc; int32_t rotate_k; double theta;
+  int32_t* mem_rows; int32_t* n_mem; uint16_t* Qr; uint16_t* Kr;
+};
+
+__device__ __forceinline__ int clamp_nsel(const int32_t* n_sel, int top_k) {
+  int ns = *n_sel;
+  return ns < 0 ? 0 : (ns > top_k ? top_k : ns);
 }
 
-// Rotates Q (rows u·Hq + h, position pos0 + M_loc − M + u) and, unless the
-// caller did, K_loc (rows v·8 + g, position pos0 + v). One thread per pair.
-__global__ __launch_bounds__(256) void rope_kernel(const uint16_t* __restrict__ Q, int32_t M,
-                                                   int32_t Hq, const uint16_t* __restrict__ Kl,
-                                                   int32_t M_loc, int32_t rotate_k, double theta,
-                                                   const int64_t* __restrict__ pos0_p,
-                                                   uint16_t* __restrict__ Qr,
-                                                   uint16_t* __restrict__ Kr) {
-  const int64_t q_pairs = (int64_t)M * Hq * 64;
-  const int64_t k_pairs = rotate_k ? (int64_t)M_loc * kHeads * 64 : 0;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+  if (blockIdx.x == 0) {
+    // ---- chunk list of the selected documents, in rank order
+    if (threadIdx.x >= 64) return;
+    const int lane = threadIdx.x;
+    const int ns = clamp_nsel(a.n_sel, a.top_k);
+    int64_t start = 0, cnt = 0;
+    if (lane < ns) {
+      const int32_t id = a.sel_ids[lane];
+      if (id >= 0 && id < a.n_docs) {
+        int64_t c0 = a.dco[id], c1 = a.dco[id + 1];
+        c0 = max((int64_t)0, min(c0, a.n_chunks));
+        c1 = max(c0, min(c1, a.n_chunks));
+        start = c0;
+        cnt = c1 - c0;
+      }
+    }
+    int64_t incl = cnt;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const int64_t off = incl - cnt;
+    const int64_t total = __shfl(incl, 63);
+    for (int64_t j = 0; j < cnt && off + j < a.max_sel; ++j)
+      a.mem_rows[off + j] = (int32_t)(start + j);
+    if (lane == 0) *a.n_mem = (int32_t)(total < a.max_sel ? total : a.max_sel);
+    return;
+  }
+  // ---- global RoPE: Q rows u·Hq + h at pos0 + (M_loc − M) + u; K rows v·8 + g at pos0 + v
+  const int64_t q_pairs = (int64_t)a.M * a.Hq * 64;
+  const int64_t k_pairs = a.rotate_k ? (int64_t)a.M_loc * kHeads * 64 : 0;
+  const int64_t idx = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x;
   if (idx >= q_pairs + k_pairs) return;
-  const int64_t pos0 = *pos0_p;
+  const int64_t pos0 = a.pos0 < 0 ? (int64_t)clamp_nsel(a.n_sel, a.top_k) : a.pos0;
   const uint16_t* src;
   uint16_t* dst;
   int64_t pos;
   int m;
   if (idx < q_pairs) {
-    const int64_t row = idx / 64;  // u * Hq + h
+    const int64_t row = idx / 64;
     m = (int)(idx % 64);
-    const int64_t u = row / Hq;
-    pos = pos0 + (M_loc - M) + u;
-    src = Q + row * kDim;
-    dst = Qr + row * kDim;
+    pos = pos0 + (a.M_loc - a.M) + row / a.Hq;
+    src = a.Q + row * kDim;
+    dst = a.Qr + row * kDim;
   } else {
     const int64_t k = idx - q_pairs;
-    const int64_t row = k / 64;  // v * 8 + g
+    const int64_t row = k / 64;
     m = (int)(k % 64);
     pos = pos0 + row / kHeads;
-    src = Kl + row * kDim;
-    dst = Kr + row * kDim;
+    src = a.Kl + row * kDim;
+    dst = a.Kr + row * kDim;
   }
-  const double om = pow(theta, -2.0 * (double)m / (double)kDim);
-  double s, c;
-  sincos((double)pos * om, &s, &c);
+  const double om = pow(a.theta, -2.0 * (double)m / (double)kDim);
+  double sn, cs;
+  sincos((double)pos * om, &sn, &cs);
   const double x = bf16f(src[m]), y = bf16f(src[m + 64]);
-  dst[m] = d2bf(x * c - y * s);
-  dst[m + 64] = d2bf(y * c + x * s);
+  dst[m] = d2bf(x * cs - y * sn);
+  dst[m + 64] = d2bf(y * cs + x * sn);
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// LDS pitches (bf16 elements): P tile [32 rows][32 keys], V^T tile [128][32].
-constexpr int kPPitch = 40;
-constexpr int kVPitch = 40;
+// LDS pitches (bf16 elements)
+constexpr int kKPitch = 136;  // K tile [32 keys][128 dims]
+constexpr int kVPitch = 40;   // V^T tile [128 dims][32 keys]
+constexpr int kPPitch = 40;   // P tile [32 rows][32 keys]
 
 __global__ __launch_bounds__(64) void attn_kernel(const uint16_t* __restrict__ Qr, int32_t M,
                                                   int32_t Hq, const uint16_t* __restrict__ Kloc,
@@ -145,8 +143,9 @@ __global__ __launch_bounds__(64) void attn_kernel(const uint16_t* __restrict__ Q
                                                   int32_t key_split, float qk_scale_log2,
                                                   float* __restrict__ Opart,
                                                   float* __restrict__ ML) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[kRowTile * kPPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kKeyTile * kKPitch];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[kDim * kVPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[kRowTile * kPPitch];
 
   const int lane = threadIdx.x;
   const int col = lane & 31;      // MFMA column lane (key / dim)
@@ -162,7 +161,7 @@ __global__ __launch_bounds__(64) void attn_kernel(const uint16_t* __restrict__ Q
   const int k_end = min(k_begin + key_split, n_keys);
   const int64_t n_rows_tot = (int64_t)M * Hq;
 
-  // A fragments of this lane's query row (row = l % 32 of the block).
+  // A fragments of this lane's query row (row = lane % 32 of the block)
   uint4 qa[8];
   {
     const int r = rb * kRowTile + col;
@@ -176,7 +175,7 @@ __global__ __launch_bounds__(64) void attn_kernel(const uint16_t* __restrict__ Q
       for (int ks = 0; ks < 8; ++ks) qa[ks] = make_uint4(0, 0, 0, 0);
     }
   }
-  // The 16 accumulator rows this lane holds: i(v) = 8(v/4) + 4·half + v%4.
+  // accumulator rows held by this lane: i(v) = 8(v/4) + 4·half + v%4
   int u_of[16];
   bool row_ok[16];
 #pragma unroll
@@ -195,57 +194,56 @@ __global__ __launch_bounds__(64) void attn_kernel(const uint16_t* __restrict__ Q
 #pragma unroll
   for (int v = 0; v < 16; ++v) { mrow[v] = -INFINITY; lpart[v] = 0.0f; }
 
+  const int sub = lane >> 4;       // row of a 4-row load group
+  const int dv = lane & 15;        // 16-byte vector within a 256-byte head row
   for (int kt = k_begin; kt < k_end; kt += kKeyTile) {
-    // ---- K fragments straight from memory: key kt + col, 16 bytes per k-step
-    uint4 kb[8];
-    {
-      const int j = kt + col;
-      const uint16_t* krow = nullptr;
-      if (j < k_end) {
-        krow = j < n_mem ? Kbar + ((int64_t)mem_rows[j] * kHeads + g) * kDim
-                         : Kloc + ((int64_t)(j - n_mem) * kHeads + g) * kDim;
-      }
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        kb[ks] = krow ? reinterpret_cast<const uint4*>(krow)[ks * 2 + half] : make_uint4(0, 0, 0, 0);
-    }
-    // ---- V tile -> LDS, transposed to [dim][key]
+    // ---- K and V tiles: 16 lanes per 256-byte row, 4 rows per instruction
+    uint4 kx[8], vx[8];
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
-      const int idx = it * 64 + lane;  // 512 vectors of 8 dims
-      const int kk = idx >> 4, dv = idx & 15;
-      const int j = kt + kk;
-      uint4 x = make_uint4(0, 0, 0, 0);
+      const int j = kt + it * 4 + sub;
+      kx[it] = vx[it] = make_uint4(0, 0, 0, 0);
       if (j < k_end) {
-        const uint16_t* vrow = j < n_mem ? Vbar + ((int64_t)mem_rows[j] * kHeads + g) * kDim
-                                         : Vloc + ((int64_t)(j - n_mem) * kHeads + g) * kDim;
-        x = reinterpret_cast<const uint4*>(vrow)[dv];
+        const int64_t off = j < n_mem ? ((int64_t)mem_rows[j] * kHeads + g) * kDim
+                                      : ((int64_t)(j - n_mem) * kHeads + g) * kDim;
+        const uint16_t* kb = j < n_mem ? Kbar : Kloc;
+        const uint16_t* vb = j < n_mem ? Vbar : Vloc;
+        kx[it] = reinterpret_cast<const uint4*>(kb + off)[dv];
+        vx[it] = reinterpret_cast<const uint4*>(vb + off)[dv];
       }
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int kk = it * 4 + sub;
+      *reinterpret_cast<uint4*>(&Ks[kk * kKPitch + dv * 8]) = kx[it];
+      const uint32_t w[4] = {vx[it].x, vx[it].y, vx[it].z, vx[it].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         Vt[(dv * 8 + 2 * e) * kVPitch + kk] = (uint16_t)(w[e] & 0xffffu);
         Vt[(dv * 8 + 2 * e + 1) * kVPitch + kk] = (uint16_t)(w[e] >> 16);
       }
     }
+    __syncthreads();
 
     // ---- S = Q K^T (rows × 32 keys)
     f32x16_t S;
 #pragma unroll
     for (int v = 0; v < 16; ++v) S[v] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[ks]), as_bf16x8(kb[ks]), S, 0, 0, 0);
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 kb = *reinterpret_cast<const uint4*>(&Ks[col * kKPitch + ks * 16 + half * 8]);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[ks]), as_bf16x8(kb), S, 0, 0, 0);
+    }
 
     // ---- mask, scale to the log2 domain, online softmax
     const int j = kt + col;
     const bool key_ok = j < k_end;
-    const int vloc = j - n_mem;  // local index when j >= n_mem
+    const int vloc = j - n_mem;
     float p[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      bool ok = key_ok && row_ok[v] && (j < n_mem || vloc <= (M_loc - M) + u_of[v]);
-      float s = ok ? S[v] * qk_scale_log2 : -INFINITY;
+      const bool ok = key_ok && row_ok[v] && (j < n_mem || vloc <= (M_loc - M) + u_of[v]);
+      const float s = ok ? S[v] * qk_scale_log2 : -INFINITY;
       float t = s;
       t = fmaxf(t, __shfl_xor(t, 1));
       t = fmaxf(t, __shfl_xor(t, 2));
@@ -316,20 +314,46 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
                                                       int32_t n_splits, int64_t n_rows,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ out_f32) {
+  __shared__ float w[kMaxSplits];
+  __shared__ float s_mx, s_L;
   const int64_t row = blockIdx.x;
   const int d = threadIdx.x;
-  float mx = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, ML[((int64_t)s * n_rows + row) * 2]);
-  float L = 0.0f, acc = 0.0f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float m = ML[((int64_t)s * n_rows + row) * 2];
-      if (m == -INFINITY) continue;
-      const float w = exp2f(m - mx);
-      L += w * ML[((int64_t)s * n_rows + row) * 2 + 1];
-      acc += w * Opart[((int64_t)s * n_rows + row) * kDim + d];
+  for (int s = d; s < n_splits; s += blockDim.x) w[s] = ML[((int64_t)s * n_rows + row) * 2];
+  __syncthreads();
+  if (d == 0) {
+    float mx = -INFINITY;
+    for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, w[s]);
+    s_mx = mx;
+  }
+  __syncthreads();
+  const float mx = s_mx;
+  for (int s = d; s < n_splits; s += blockDim.x) {
+    const float m = w[s];
+    w[s] = (mx == -INFINITY || m == -INFINITY) ? 0.0f : exp2f(m - mx);
+  }
+  __syncthreads();
+  if (d == 0) {
+    float L = 0.0f;
+    for (int s = 0; s < n_splits; ++s)
+      if (w[s] != 0.0f) L += w[s] * ML[((int64_t)s * n_rows + row) * 2 + 1];
+    s_L = L;
+  }
+  float acc = 0.0f;
+  for (int s0 = 0; s0 < n_splits; s0 += 8) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u;
+      x[u] = (s < n_splits && w[s] != 0.0f) ? Opart[((int64_t)s * n_rows + row) * kDim + d] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u;
+      if (s < n_splits) acc += w[s] * x[u];
     }
   }
+  __syncthreads();
+  const float L = s_L;
   const float o = L > 0.0f ? acc / L : 0.0f;
   out[row * kDim + d] = f2bf(o);
   if (out_f32) out_f32[row * kDim + d] = o;
@@ -337,7 +361,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
 
 struct AttnPlan {
   int32_t row_blocks, key_split, n_splits;
-  size_t off_rows, off_nmem, off_pos0, off_qr, off_kr, off_opart, off_ml, total;
+  size_t off_rows, off_nmem, off_qr, off_kr, off_opart, off_ml, total;
 };
 
 AttnPlan attn_plan(int32_t M, int32_t M_loc, int32_t Hq, int64_t max_sel) {
@@ -345,19 +369,20 @@ AttnPlan attn_plan(int32_t M, int32_t M_loc, int32_t Hq, int64_t max_sel) {
   const int32_t G = Hq / kHeads;
   p.row_blocks = (M * G + kRowTile - 1) / kRowTile;
   const int64_t max_keys = max_sel + M_loc;
-  // aim for >= 512 waves in flight across the chip
+  // aim for >= 512 waves in flight across the chip, at most kMaxSplits splits
   int64_t want = 512 / ((int64_t)p.row_blocks * kHeads);
   if (want < 1) want = 1;
-  int64_t tiles = (max_keys + kKeyTile - 1) / kKeyTile;
+  const int64_t tiles = (max_keys + kKeyTile - 1) / kKeyTile;
   int64_t tiles_per_split = (tiles + want - 1) / want;
   if (tiles_per_split < 1) tiles_per_split = 1;
+  if ((tiles + tiles_per_split - 1) / tiles_per_split > kMaxSplits)
+    tiles_per_split = (tiles + kMaxSplits - 1) / kMaxSplits;
   p.key_split = (int32_t)(tiles_per_split * kKeyTile);
   p.n_splits = (int32_t)((max_keys + p.key_split - 1) / p.key_split);
   if (p.n_splits < 1) p.n_splits = 1;
   size_t o = 0;
   p.off_rows = o; o = align_up(o + sizeof(int32_t) * (size_t)(max_sel > 0 ? max_sel : 1), 256);
   p.off_nmem = o; o = align_up(o + sizeof(int32_t), 256);
-  p.off_pos0 = o; o = align_up(o + sizeof(int64_t), 256);
   p.off_qr = o; o = align_up(o + 2 * (size_t)M * Hq * kDim, 256);
   p.off_kr = o; o = align_up(o + 2 * (size_t)M_loc * kHeads * kDim, 256);
   p.off_opart = o; o = align_up(o + 4 * (size_t)p.n_splits * M * Hq * kDim, 256);
@@ -379,23 +404,24 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s)
   AttnWs w;
   w.mem_rows = reinterpret_cast<int32_t*>(base + p.off_rows);
   w.n_mem = reinterpret_cast<int32_t*>(base + p.off_nmem);
-  w.pos0 = reinterpret_cast<int64_t*>(base + p.off_pos0);
   w.Qr = reinterpret_cast<uint16_t*>(base + p.off_qr);
   w.Kr = reinterpret_cast<uint16_t*>(base + p.off_kr);
   w.Opart = reinterpret_cast<float*>(base + p.off_opart);
   w.ML = reinterpret_cast<float*>(base + p.off_ml);
 
-  hipLaunchKernelGGL(assemble_kernel, dim3(1), dim3(64), 0, s, a.sel_ids, a.n_sel, a.top_k, a.dco,
-                     a.n_docs, a.n_chunks, a.max_sel_chunks, a.pos0, w.mem_rows, w.n_mem, w.pos0);
-  MSA_LAUNCH_CHECK("assemble_kernel launch");
+  PrepArgs pa;
+  pa.sel_ids = a.sel_ids; pa.n_sel = a.n_sel; pa.top_k = a.top_k;
+  pa.dco = a.dco; pa.n_docs = a.n_docs; pa.n_chunks = a.n_chunks;
+  pa.max_sel = a.max_sel_chunks; pa.pos0 = a.pos0;
+  pa.Q = a.Q; pa.M = a.M; pa.Hq = a.n_q_heads;
+  pa.Kl = a.K_loc; pa.M_loc = a.M_loc; pa.rotate_k = a.k_loc_rotated ? 0 : 1; pa.theta = a.theta;
+  pa.mem_rows = w.mem_rows; pa.n_mem = w.n_mem; pa.Qr = w.Qr; pa.Kr = w.Kr;
+  const int64_t pairs = (int64_t)a.M * a.n_q_heads * 64 +
+                        (pa.rotate_k ? (int64_t)a.M_loc * kHeads * 64 : 0);
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(1 + (pairs + 255) / 256)), dim3(256), 0, s, pa);
+  MSA_LAUNCH_CHECK("prep_kernel launch");
 
-  const int rotate_k = a.k_loc_rotated ? 0 : 1;
-  const int64_t pairs = (int64_t)a.M * a.n_q_heads * 64 + (rotate_k ? (int64_t)a.M_loc * kHeads * 64 : 0);
-  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s, a.Q, a.M,
-                     a.n_q_heads, a.K_loc, a.M_loc, rotate_k, a.theta, w.pos0, w.Qr, w.Kr);
-  MSA_LAUNCH_CHECK("rope_kernel launch");
-
-  const uint16_t* kloc = rotate_k ? w.Kr : a.K_loc;
+  const uint16_t* kloc = pa.rotate_k ? w.Kr : a.K_loc;
   const float scale = (float)(1.0 / sqrt((double)kDim)) * kLog2e;
   hipLaunchKernelGGL(attn_kernel, dim3(p.row_blocks, kHeads, p.n_splits), dim3(64), 0, s, w.Qr,
                      a.M, a.n_q_heads, kloc, a.V_loc, a.M_loc, a.Kbar, a.Vbar, w.mem_rows, w.n_mem,

@@ -78,38 +78,62 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// q̂ = x / max(‖x‖, eps) (fp64) for the 16 dims [16(l%8), +16) of head l/8
-// held by this lane (the head's other dims sit in the 7 neighbouring lanes of
-// the same group of 8), returned as bf16 hi + lo vectors of 8 dims each.
-__device__ inline void qhat_hilo16(const uint16_t* row, int lane, uint4* hi, uint4* lo) {
-  const uint4* src = reinterpret_cast<const uint4*>(row) + 2 * lane;
-  const uint4 a = src[0], b = src[1];
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  double x[16];
-  double ss = 0.0;
+// Cross-lane sums with DPP (full VALU rate, no LDS traffic).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+// Sum over the 16 lanes of each row; every lane of the row gets the sum.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
+  return x;
+}
+// Given row sums in every lane, lane 63 gets the sum over the four rows.
+__device__ __forceinline__ float rows_to_lane63(float x) {
+  x += dpp_f<0x142, 0xA>(x);  // row_bcast15 into rows 1 and 3
+  x += dpp_f<0x143, 0xC>(x);  // row_bcast31 into rows 2 and 3
+  return x;
+}
+
+// Router-query slice held by lane l in the coalesced scan layout: the 16-byte
+// vectors l and 64+l of a 1024-element row, i.e. dims [8(l%16), +8) of heads
+// l/16 and 4 + l/16. Returns q̂ = x / max(‖x‖, eps) (fp64 norm per head) as
+// bf16 hi + lo vectors: [0] head l/16, [1] head 4 + l/16.
+__device__ inline void qhat_hilo_pair(const uint16_t* row, int lane, uint4* hi, uint4* lo) {
+  const uint4* src = reinterpret_cast<const uint4*>(row);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    x[2 * i] = bf16lo(w[i]);
-    x[2 * i + 1] = bf16hi(w[i]);
-    ss += x[2 * i] * x[2 * i] + x[2 * i + 1] * x[2 * i + 1];
-  }
-  ss += __shfl_xor(ss, 1);
-  ss += __shfl_xor(ss, 2);
-  ss += __shfl_xor(ss, 4);
-  const double nrm = sqrt(ss);
-  const double inv = 1.0 / (nrm > (double)kNormEps ? nrm : (double)kNormEps);
-  uint32_t h[8], l[8];
+  for (int p = 0; p < 2; ++p) {
+    const uint4 a = src[64 * p + lane];
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+    double x[8];
+    double ss = 0.0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const double q0 = x[2 * i] * inv, q1 = x[2 * i + 1] * inv;
-    const uint16_t h0 = d2bf(q0), h1 = d2bf(q1);
-    h[i] = pack2(h0, h1);
-    l[i] = pack2(d2bf(q0 - (double)bf16f(h0)), d2bf(q1 - (double)bf16f(h1)));
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16lo(w[i]);
+      x[2 * i + 1] = bf16hi(w[i]);
+      ss += x[2 * i] * x[2 * i] + x[2 * i + 1] * x[2 * i + 1];
+    }
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 4);
+    ss += __shfl_xor(ss, 8);
+    const double nrm = sqrt(ss);
+    const double inv = 1.0 / (nrm > (double)kNormEps ? nrm : (double)kNormEps);
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double q0 = x[2 * i] * inv, q1 = x[2 * i + 1] * inv;
+      const uint16_t h0 = d2bf(q0), h1 = d2bf(q1);
+      h[i] = pack2(h0, h1);
+      l[i] = pack2(d2bf(q0 - (double)bf16f(h0)), d2bf(q1 - (double)bf16f(h1)));
+    }
+    hi[p] = make_uint4(h[0], h[1], h[2], h[3]);
+    lo[p] = make_uint4(l[0], l[1], l[2], l[3]);
   }
-  hi[0] = make_uint4(h[0], h[1], h[2], h[3]);
-  hi[1] = make_uint4(h[4], h[5], h[6], h[7]);
-  lo[0] = make_uint4(l[0], l[1], l[2], l[3]);
-  lo[1] = make_uint4(l[4], l[5], l[6], l[7]);
 }
 
 // Order-preserving map of a float onto uint32 (larger float -> larger key).

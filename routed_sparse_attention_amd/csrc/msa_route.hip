@@ -15,11 +15,14 @@
 //     (q̂ ≈ hi + lo to ~2^-17), so bf16 products against the bf16 keys keep
 //     fp32-level accuracy.
 //   scan_valu (decode and small batches, <= 8 rows per tile): HBM-bound
-//     stream. Lane l of a wave owns head l/8, dims [16(l%8), 16(l%8)+16) of
-//     one chunk; it keeps its slice of every tile row's q̂ in registers for
-//     the whole launch. Per chunk: two 16-byte loads, v_dot2 bf16 products for
-//     q̂·k (hi and lo) and k·k, an 8-lane reduction per head, a per-head
-//     1/max(‖k‖, eps) scale and an 8-group reduction over heads.
+//     stream, one chunk row (2 KiB) per wave per step. Lane l loads the 16-byte
+//     vectors l and 64+l of the row — each load instruction covers one
+//     contiguous KiB — i.e. dims [8(l%16), +8) of heads l/16 and 4 + l/16, and
+//     keeps the matching slice of every tile row's q̂ in registers for the
+//     whole launch. Per chunk: v_dot2 bf16 products for q̂·k (hi and lo) and
+//     k·k, DPP sums over each 16-lane row (one head pair per row),
+//     1/max(‖k‖, eps) by v_rsq, and a DPP row broadcast that leaves the head
+//     sum in lane 63.
 //   scan_mfma (batched rows): msa_route_mfma.hip.
 #include "msa_internal.h"
 
@@ -63,19 +66,20 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const uint16_t* __restri
   const int wave = threadIdx.x >> 6;
   const TileRows tr = tile_rows_of(g, blockIdx.y);
   const int n_rows = tr.nq * tr.nr;  // <= R
-  // this lane's slice of every tile row's q̂ (hi and lo, two 16-byte vectors each)
+  // this lane's slice of every tile row's q̂: [k][0] head lane/16, [k][1] head 4 + lane/16
   uint4 qh[R][2], ql[R][2];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     if (k < n_rows) {
       const int64_t row = (int64_t)(tr.b0 + k / tr.nr) * g.M + tr.m0 + k % tr.nr;
-      qhat_hilo16(QR + row * kRowElems, lane, qh[k], ql[k]);
+      qhat_hilo_pair(QR + row * kRowElems, lane, qh[k], ql[k]);
     } else {
       qh[k][0] = qh[k][1] = ql[k][0] = ql[k][1] = make_uint4(0, 0, 0, 0);
     }
   }
   const bool mean = token_reduce == MSA_TOKEN_REDUCE_MEAN;
   const float fin = (mean && g.parts == 1) ? 1.0f / (float)g.M : 1.0f;
+  const float eps2 = kNormEps * kNormEps;
   const int64_t wave_id = (int64_t)blockIdx.x * kScanWaves + wave;
   const int64_t n_waves = (int64_t)gridDim.x * kScanWaves;
 
@@ -85,8 +89,8 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const uint16_t* __restri
     for (int u = 0; u < kScanUnroll; ++u) {
       const int64_t c = c0 + u;
       if (c < n_chunks) {
-        k0[u] = load_stream(KR + c * kRowVec + 2 * lane);
-        k1[u] = load_stream(KR + c * kRowVec + 2 * lane + 1);
+        k0[u] = load_stream(KR + c * kRowVec + lane);
+        k1[u] = load_stream(KR + c * kRowVec + 64 + lane);
       } else {
         k0[u] = k1[u] = make_uint4(0, 0, 0, 0);
       }
@@ -94,38 +98,39 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const uint16_t* __restri
 #pragma unroll
     for (int u = 0; u < kScanUnroll; ++u) {
       const int64_t c = c0 + u;
-      const uint32_t kw[8] = {k0[u].x, k0[u].y, k0[u].z, k0[u].w,
-                              k1[u].x, k1[u].y, k1[u].z, k1[u].w};
-      float nrm = 0.0f;
+      const uint32_t ka[4] = {k0[u].x, k0[u].y, k0[u].z, k0[u].w};
+      const uint32_t kb[4] = {k1[u].x, k1[u].y, k1[u].z, k1[u].w};
+      float na = 0.0f, nb = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) nrm = dot2(kw[i], kw[i], nrm);
-      nrm += __shfl_xor(nrm, 1);
-      nrm += __shfl_xor(nrm, 2);
-      nrm += __shfl_xor(nrm, 4);
-      const float kn = sqrtf(nrm);
-      const float inv_k = 1.0f / (kn > kNormEps ? kn : kNormEps);
+      for (int i = 0; i < 4; ++i) {
+        na = dot2(ka[i], ka[i], na);
+        nb = dot2(kb[i], kb[i], nb);
+      }
+      const float ia = __builtin_amdgcn_rsqf(fmaxf(row_sum16(na), eps2));
+      const float ib = __builtin_amdgcn_rsqf(fmaxf(row_sum16(nb), eps2));
       float red[R];
 #pragma unroll
       for (int k = 0; k < R; ++k) {
-        const uint32_t hw[8] = {qh[k][0].x, qh[k][0].y, qh[k][0].z, qh[k][0].w,
-                                qh[k][1].x, qh[k][1].y, qh[k][1].z, qh[k][1].w};
-        const uint32_t lw[8] = {ql[k][0].x, ql[k][0].y, ql[k][0].z, ql[k][0].w,
-                                ql[k][1].x, ql[k][1].y, ql[k][1].z, ql[k][1].w};
-        float d = 0.0f;
+        const uint32_t ha[4] = {qh[k][0].x, qh[k][0].y, qh[k][0].z, qh[k][0].w};
+        const uint32_t hb[4] = {qh[k][1].x, qh[k][1].y, qh[k][1].z, qh[k][1].w};
+        const uint32_t la[4] = {ql[k][0].x, ql[k][0].y, ql[k][0].z, ql[k][0].w};
+        const uint32_t lb[4] = {ql[k][1].x, ql[k][1].y, ql[k][1].z, ql[k][1].w};
+        float da = 0.0f, db = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) d = dot2(lw[i], kw[i], d);
+        for (int i = 0; i < 4; ++i) {
+          da = dot2(la[i], ka[i], da);
+          db = dot2(lb[i], kb[i], db);
+        }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) d = dot2(hw[i], kw[i], d);
-        d += __shfl_xor(d, 1);
-        d += __shfl_xor(d, 2);
-        d += __shfl_xor(d, 4);
-        float sh = d * inv_k;  // cosine of this head (q̂ is unit)
-        sh += __shfl_xor(sh, 8);
-        sh += __shfl_xor(sh, 16);
-        sh += __shfl_xor(sh, 32);
-        red[k] = sh * 0.125f;  // mean over the 8 heads
+        for (int i = 0; i < 4; ++i) {
+          da = dot2(ha[i], ka[i], da);
+          db = dot2(hb[i], kb[i], db);
+        }
+        // cosines of heads lane/16 and 4 + lane/16 (q̂ is unit), summed over rows
+        const float sh = row_sum16(da) * ia + row_sum16(db) * ib;
+        red[k] = rows_to_lane63(sh) * 0.125f;  // mean over the 8 heads (lane 63)
       }
-      // reduce each query's rows (max, or sum for MEAN) and store
+      // reduce each query's rows (max, or sum for MEAN); lane 63 stores
       float v = 0.0f;
 #pragma unroll
       for (int k = 0; k < R; ++k) {
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const uint16_t* __restri
           const int m = k % tr.nr;
           const float x = red[k];
           v = (m == 0) ? x : (mean ? v + x : nan_max(v, x));
-          if (m == tr.nr - 1 && lane == 0 && c < n_chunks)
+          if (m == tr.nr - 1 && lane == 63 && c < n_chunks)
             out[((int64_t)tr.part * g.B + tr.b0 + k / tr.nr) * n_chunks + c] = v * fin;
         }
       }
@@ -171,7 +176,8 @@ int launch_scan_valu(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRb
   if (wg > 2048) wg = 2048;
   const dim3 grid((unsigned)wg, (unsigned)g.n_tiles);
   const uint4* kr = reinterpret_cast<const uint4*>(KRbar);
-  const int rows = g.parts == 1 ? g.q_per_tile * g.M : g.tile_rows;
+  // rows actually present in a tile (a lone decode query must not pay for 8)
+  const int rows = g.parts == 1 ? (g.q_per_tile < g.B ? g.q_per_tile : g.B) * g.M : g.tile_rows;
   if (rows <= 1)
     hipLaunchKernelGGL(scan_valu_kernel<1>, grid, dim3(256), 0, s, QR, g, kr, n_chunks, token_reduce, out);
   else if (rows <= 2)

@@ -6,117 +6,252 @@
 // Readings: ties go to the lowest document id; with fewer than k documents
 // all are selected; a NaN score ranks below every number.
 //
-// Design. Every document score becomes one unique 64-bit key
-//   (order-preserving uint32 of the score) << 32 | (0xFFFFFFFF − id),
-// so "larger key" means "better document", equal scores fall back to the
-// lower id, and selection is a plain descending sort of integers — the result
-// is deterministic and independent of thread order.
-//   stage 1: one workgroup per (slice of 1024 documents, query): each thread
-//     max-reduces its documents' chunk ranges, max-merges with the previous
-//     scores when accumulating, writes the document scores, and the workgroup
-//     sorts its 1024 keys (bitonic, in LDS) and keeps its k best;
-//   stage 2: one workgroup per query merges the slices' candidates the same
-//     way and writes ids, scores and n_sel.
+// Design.
+//   doc_max: one thread per (document, query); each thread reads its chunk
+//     range with 8 independent loads in flight and max-reduces it (NaN
+//     propagates, as numpy's max does), max-merges with the previous score
+//     when accumulating, and writes the document score.
+//   topk_select: one 1024-thread workgroup per query. Each document becomes
+//     the unique 64-bit key (order-preserving uint32 of the score) << 32 |
+//     (0xFFFFFFFF − id), so larger key = better document and equal scores
+//     fall back to the lower id (NaN maps to the lowest scores).
+//     Fast path (k <= 16): every wave takes the maximum key of its share;
+//     the smallest of the 16 wave maxima is a lower bound on the k-th best
+//     key (16 distinct keys reach it), so only keys at or above it — a few
+//     dozen on real data — are appended (ballot-compacted) to an LDS list,
+//     which is bitonic-sorted; its head is the answer.
+//     Fallback (more than 2048 candidates, i.e. massive ties, or k > 16):
+//     radix select on the uint32 score keys. Four passes
+//     over 8-bit digits, most significant first, histogram the keys that
+//     share the digits fixed so far (one LDS histogram per wave, rows padded
+//     so waves hit different banks) and fix the digit holding the k-th best;
+//     after the last pass T is the k-th best key exactly. Every key above T is
+//     selected, then the lowest-index keys equal to T (a ballot scan over
+//     rounds of 1024 consecutive indices fixes that order). The k
+//     winners are ranked by (key desc, id asc) with a k×k comparison, so the
+//     output does not depend on thread timing.
 #include "msa_internal.h"
 
 namespace msa {
 namespace {
 
-constexpr int kSortN = 1024;
-constexpr int kThreads = 256;
+constexpr int kMaxThreads = 256;
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kHistPitch = 257;
+constexpr int kMaxK = 64;
+constexpr int kCandCap = 2048;
 
-// Sorts 1024 keys in LDS into descending order (all 256 threads take part).
-__device__ void bitonic_desc_1024(uint64_t* s) {
-  const int tid = threadIdx.x;
-  for (int k = 2; k <= kSortN; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-#pragma unroll
-      for (int p = tid; p < kSortN / 2; p += kThreads) {
-        const int i = 2 * j * (p / j) + (p % j);
-        const int l = i + j;
-        const bool desc = (i & k) == 0;
-        const uint64_t x = s[i], y = s[l];
-        if (desc ? (x < y) : (x > y)) {
-          s[i] = y;
-          s[l] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
-__device__ __forceinline__ uint64_t doc_key(float s, int32_t i) {
-  return ((uint64_t)ord_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
-}
-
-__global__ __launch_bounds__(256) void doc_topk1_kernel(const float* __restrict__ S, int64_t C,
-                                                        const int64_t* __restrict__ dco,
-                                                        int32_t n_docs,
-                                                        float* __restrict__ doc_scores,
-                                                        int32_t accumulate, int32_t K,
-                                                        uint64_t* __restrict__ cand,
-                                                        int32_t n_slices) {
-  __shared__ uint64_t keys[kSortN];
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(256) void doc_max_kernel(const float* __restrict__ S, int64_t C,
+                                                      const int64_t* __restrict__ dco,
+                                                      int32_t n_docs,
+                                                      float* __restrict__ doc_scores,
+                                                      int32_t accumulate) {
   const int b = blockIdx.y;
-  const int slice = blockIdx.x;
-  for (int q = 0; q < kSortN / kThreads; ++q) {
-    const int64_t i = (int64_t)slice * kSortN + q * kThreads + tid;
-    uint64_t key = 0;
-    if (i < n_docs) {
-      int64_t c0 = dco[i], c1 = dco[i + 1];
-      c0 = max((int64_t)0, min(c0, C));
-      c1 = max(c0, min(c1, C));
-      float s = -INFINITY;
-      const float* Sb = S + (int64_t)b * C;
-      for (int64_t c = c0; c < c1; ++c) s = (c == c0) ? Sb[c] : nan_max(s, Sb[c]);
-      float* ds = doc_scores + (int64_t)b * n_docs + i;
-      if (accumulate) s = nan_max(*ds, s);
-      *ds = s;
-      key = doc_key(s, (int32_t)i);
-    }
-    keys[q * kThreads + tid] = key;
+  const int64_t i = (int64_t)blockIdx.x * kMaxThreads + threadIdx.x;
+  if (i >= n_docs) return;
+  int64_t c0 = dco[i], c1 = dco[i + 1];
+  c0 = max((int64_t)0, min(c0, C));
+  c1 = max(c0, min(c1, C));
+  const float* Sb = S + (int64_t)b * C;
+  float s = -INFINITY;
+  for (int64_t c = c0; c < c1; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (c + u < c1) ? Sb[c + u] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s = nan_max(s, v[u]);
   }
-  __syncthreads();
-  bitonic_desc_1024(keys);
-  if (tid < K) cand[((int64_t)b * n_slices + slice) * K + tid] = keys[tid];
+  float* ds = doc_scores + (int64_t)b * n_docs + i;
+  if (accumulate) s = nan_max(*ds, s);
+  *ds = s;
 }
 
-__global__ __launch_bounds__(256) void doc_topk2_kernel(const uint64_t* __restrict__ cand,
-                                                        int32_t n_slices, int32_t K,
-                                                        int32_t n_docs,
-                                                        int32_t* __restrict__ topk_ids,
-                                                        float* __restrict__ topk_scores,
-                                                        int32_t* __restrict__ n_sel) {
-  __shared__ uint64_t keys[kSortN];
-  const int tid = threadIdx.x;
-  const int b = blockIdx.x;
-  const int64_t total = (int64_t)n_slices * K;
-  const uint64_t* src = cand + (int64_t)b * total;
-  if (tid < K) keys[tid] = 0;
-  const int fresh = kSortN - K;
-  for (int64_t base = 0; base < total || base == 0; base += fresh) {
-    for (int j = K + tid; j < kSortN; j += kThreads) {
-      const int64_t idx = base + (j - K);
-      keys[j] = idx < total ? src[idx] : 0;
+// Radix-select fallback: fills sel[0..Ks) with the Ks best 64-bit keys (any
+// order). All 1024 threads must call it.
+__device__ void radix_select(const float* __restrict__ s, int N, int Ks, uint32_t* hist,
+                             uint32_t* tot, uint32_t* wave_eq, uint64_t* sel, int* sel_n,
+                             uint32_t* scratch) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  uint32_t& s_digit = scratch[0];
+  uint32_t& s_krem = scratch[1];
+  uint32_t& n_eq = scratch[2];
+  uint32_t prefix = 0;           // digits fixed so far
+  uint32_t krem = (uint32_t)Ks;  // how many still to take at or below the prefix
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < kSelWaves * kHistPitch; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < N; i += kSelThreads) {
+      const uint32_t key = ord_key(s[i]);
+      const bool match = pass == 0 || (key >> (shift + 8)) == prefix;
+      if (match) atomicAdd(&hist[wave * kHistPitch + ((key >> shift) & 255u)], 1u);
     }
     __syncthreads();
-    bitonic_desc_1024(keys);
-    if (base + fresh >= total) break;
+    if (tid < 256) {
+      uint32_t c = 0;
+      for (int w = 0; w < kSelWaves; ++w) c += hist[w * kHistPitch + tid];
+      tot[tid] = c;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t acc = 0;
+      int d = 255;
+      for (; d > 0; --d) {
+        if (acc + tot[d] >= krem) break;
+        acc += tot[d];
+      }
+      s_digit = (uint32_t)d;
+      s_krem = krem - acc;
+    }
+    __syncthreads();
+    prefix = (prefix << 8) | s_digit;
+    krem = s_krem;
+    __syncthreads();
   }
-  const int ns = n_docs < K ? n_docs : K;
+  const uint32_t T = prefix;  // the Ks-th best score key; take `krem` of the keys equal to T
+
+  // Keys above T are all taken. Keys equal to T: usually exactly `krem`
+  // exist and all are taken; if more tie, the lowest indices win, found by an
+  // ordered ballot scan over rounds of 1024 consecutive indices.
+  if (tid == 0) { *sel_n = 0; n_eq = 0; }
+  __syncthreads();
+  for (int i = tid; i < N; i += kSelThreads) {
+    const uint32_t key = ord_key(s[i]);
+    if (key > T) {
+      const int slot = atomicAdd(sel_n, 1);
+      if (slot < kMaxK) sel[slot] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+    }
+    const uint64_t eqm = __ballot(key == T);
+    if (lane == 0 && eqm) atomicAdd(&n_eq, (uint32_t)__popcll(eqm));
+  }
+  __syncthreads();
+  const bool all_ties = n_eq <= krem;
+  uint32_t carry = 0;
+  for (int base = 0; base < N && carry < krem; base += kSelThreads) {
+    const int i = base + tid;
+    const uint32_t key = i < N ? ord_key(s[i]) : 0u;
+    const bool eq = i < N && key == T;
+    const uint64_t m = __ballot(eq);
+    if (lane == 0) wave_eq[wave] = (uint32_t)__popcll(m);
+    __syncthreads();
+    uint32_t before = carry, total = 0;
+    for (int w = 0; w < kSelWaves; ++w) {
+      if (w < wave) before += wave_eq[w];
+      total += wave_eq[w];
+    }
+    before += (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+    if (eq && (all_ties || before < krem)) {
+      const int slot = atomicAdd(sel_n, 1);
+      if (slot < kMaxK) sel[slot] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+    }
+    carry += total;
+    __syncthreads();
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t doc_key(float score, int i) {
+  return ((uint64_t)ord_key(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+}
+
+__global__ __launch_bounds__(1024) void topk_select_kernel(const float* __restrict__ doc_scores,
+                                                           int32_t N, int32_t K,
+                                                           int32_t* __restrict__ topk_ids,
+                                                           float* __restrict__ topk_scores,
+                                                           int32_t* __restrict__ n_sel) {
+  __shared__ uint64_t cand[kCandCap];
+  __shared__ uint64_t wmax[kSelWaves];
+  __shared__ uint32_t hist[kSelWaves * kHistPitch];
+  __shared__ uint32_t tot[256];
+  __shared__ uint32_t wave_eq[kSelWaves];
+  __shared__ uint32_t scratch[4];
+  __shared__ int n_cand;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b = blockIdx.x;
+  const float* s = doc_scores + (int64_t)b * N;
+  const int Ks = N < K ? N : K;
+
+  int cnt = kCandCap + 1;  // forces the fallback unless the fast path applies
+  if (K <= kSelWaves) {
+    uint64_t best = 0;
+    for (int i = tid; i < N; i += kSelThreads) {
+      const uint64_t k = doc_key(s[i], i);
+      best = k > best ? k : best;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint64_t y = shfl_xor_u64(best, o);
+      best = y > best ? y : best;
+    }
+    if (lane == 0) wmax[wave] = best;
+    if (tid == 0) n_cand = 0;
+    __syncthreads();
+    uint64_t T = ~0ull;
+    for (int w = 0; w < kSelWaves; ++w) T = wmax[w] < T ? wmax[w] : T;  // 0 if a wave had no keys
+    for (int i = tid; i < N; i += kSelThreads) {
+      const uint64_t k = doc_key(s[i], i);
+      const bool c = k >= T;
+      const uint64_t m = __ballot(c);
+      if (m) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&n_cand, (int)__popcll(m));
+        base = __shfl(base, 0);
+        const int pos = base + (int)__popcll(m & ((1ull << lane) - 1ull));
+        if (c && pos < kCandCap) cand[pos] = k;
+      }
+    }
+    __syncthreads();
+    cnt = n_cand;
+  }
+  if (cnt <= kCandCap) {
+    int n2 = 1;
+    while (n2 < cnt) n2 <<= 1;
+    for (int i = cnt + tid; i < n2; i += kSelThreads) cand[i] = 0;
+    __syncthreads();
+    for (int k = 2; k <= n2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int p = tid; p < n2 / 2; p += kSelThreads) {
+          const int i = 2 * j * (p / j) + (p % j);
+          const int l = i + j;
+          const bool desc = (i & k) == 0;
+          const uint64_t x = cand[i], y = cand[l];
+          if (desc ? (x < y) : (x > y)) { cand[i] = y; cand[l] = x; }
+        }
+        __syncthreads();
+      }
+    }
+  } else {
+    // massive ties or k > 16: radix select into cand[0..Ks), then rank
+    radix_select(s, N, Ks, hist, tot, wave_eq, cand + kMaxK, &n_cand, scratch);
+    if (tid < Ks) {
+      const uint64_t e = cand[kMaxK + tid];
+      int rank = 0;
+      for (int j = 0; j < Ks; ++j) rank += cand[kMaxK + j] > e ? 1 : 0;
+      cand[rank] = e;
+    }
+    __syncthreads();
+  }
   if (tid < K) {
-    const uint64_t key = keys[tid];
-    if (tid < ns) {
-      topk_ids[(int64_t)b * K + tid] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
-      topk_scores[(int64_t)b * K + tid] = ord_val((uint32_t)(key >> 32));
+    int32_t* ids = topk_ids + (int64_t)b * K;
+    float* sc = topk_scores + (int64_t)b * K;
+    if (tid < Ks) {
+      const uint64_t e = cand[tid];
+      ids[tid] = (int32_t)(0xFFFFFFFFu - (uint32_t)(e & 0xFFFFFFFFu));
+      sc[tid] = ord_val((uint32_t)(e >> 32));
     } else {
-      topk_ids[(int64_t)b * K + tid] = -1;
-      topk_scores[(int64_t)b * K + tid] = -INFINITY;
+      ids[tid] = -1;
+      sc[tid] = -INFINITY;
     }
   }
-  if (tid == 0) n_sel[b] = ns;
+  if (tid == 0) n_sel[b] = Ks;
 }
 
 __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
@@ -128,21 +263,23 @@ __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
 }  // namespace
 
 size_t doc_topk_workspace(int32_t B, int32_t n_docs, int32_t top_k) {
-  const int64_t n_slices = (n_docs + kSortN - 1) / kSortN;
-  return align_up((size_t)B * n_slices * top_k * sizeof(uint64_t), 256);
+  (void)B; (void)n_docs; (void)top_k;
+  return 0;
 }
 
 int launch_doc_topk(const float* S, int32_t B, int64_t n_chunks, const int64_t* dco,
                     int32_t n_docs, float* doc_scores, int32_t accumulate, int32_t top_k,
                     uint64_t* cand, int32_t* topk_ids, float* topk_scores, int32_t* n_sel,
                     hipStream_t s) {
-  const int32_t n_slices = (n_docs + kSortN - 1) / kSortN;
-  hipLaunchKernelGGL(doc_topk1_kernel, dim3(n_slices, B), dim3(kThreads), 0, s, S, n_chunks, dco,
-                     n_docs, doc_scores, accumulate, top_k, cand, n_slices);
-  MSA_LAUNCH_CHECK("doc_topk1_kernel launch");
-  hipLaunchKernelGGL(doc_topk2_kernel, dim3(B), dim3(kThreads), 0, s, cand, n_slices, top_k,
-                     n_docs, topk_ids, topk_scores, n_sel);
-  MSA_LAUNCH_CHECK("doc_topk2_kernel launch");
+  (void)cand;
+  if (top_k > kMaxK) return fail(MSA_ERR_UNSUPPORTED, "top_k > %d", kMaxK);
+  const unsigned blocks = (unsigned)((n_docs + kMaxThreads - 1) / kMaxThreads);
+  hipLaunchKernelGGL(doc_max_kernel, dim3(blocks, B), dim3(kMaxThreads), 0, s, S, n_chunks, dco,
+                     n_docs, doc_scores, accumulate);
+  MSA_LAUNCH_CHECK("doc_max_kernel launch");
+  hipLaunchKernelGGL(topk_select_kernel, dim3(B), dim3(kSelThreads), 0, s, doc_scores, n_docs,
+                     top_k, topk_ids, topk_scores, n_sel);
+  MSA_LAUNCH_CHECK("topk_select_kernel launch");
   return MSA_OK;
 }
 

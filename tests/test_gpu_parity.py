@@ -352,3 +352,29 @@ def test_select_topk_exact_on_given_scores():
         exp_ids, exp_sc, _ = O.topk(s, 16)
         assert list(ids[b].cpu().numpy()) == list(exp_ids)      # bit-exact, ties included
         assert int(ns[b]) == 16
+
+
+@pytest.mark.parametrize("case", ["all_equal", "k40", "small_n"])
+def test_select_topk_fallback_paths(case):
+    _banner(f"select_topk fallback {case}")
+    rng = synth.np_rng(93, 0)
+    n_docs = {"all_equal": 5000, "k40": 3000, "small_n": 7}[case]
+    counts = rng.integers(1, 9, size=n_docs)
+    dco_h = synth.offsets_from_lengths(counts)
+    C = int(dco_h[-1])
+    if case == "all_equal":
+        S = np.full((2, C), 0.25, np.float32)            # every document ties
+    else:
+        S = (rng.integers(-50, 50, size=(2, C)) / 50.0).astype(np.float32)
+    k = 40 if case == "k40" else 16
+    d = msa.dims(top_k=k)
+    ds, ids, sc, ns = msa.select_topk(torch.from_numpy(S).to(DEV), torch.from_numpy(dco_h).to(DEV), d)
+    torch.cuda.synchronize()
+    for b in range(2):
+        s = O.doc_scores(S[b].astype(np.float64), dco_h)
+        exp_ids, exp_sc, _ = O.topk(s, k)
+        n = len(exp_ids)
+        assert int(ns[b]) == n
+        assert list(ids[b].cpu().numpy()[:n]) == list(exp_ids)
+        assert np.array_equal(sc[b].cpu().numpy()[:n].astype(np.float64), exp_sc)
+        assert all(x == -1 for x in ids[b].cpu().numpy()[n:])

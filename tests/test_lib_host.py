@@ -88,6 +88,6 @@ def test_workspace_sizes():
     d = msa.dims()
     a = msa.route_topk_workspace(1, 1, 1_562_500, 46_000, d)
     b = msa.route_topk_workspace(64, 1, 250_000, 7_350, d)
-    assert a > 1_562_500 * 4 and b > 64 * 250_000 * 4
+    assert a >= 1_562_500 * 4 and b >= 64 * 250_000 * 4
     assert msa.sparse_attend_workspace(1, 129, 1024, d) > 0
     assert msa.lib().msa_route_topk_workspace(ctypes.byref(d), 0, 1, 10, 2) == 0
