@@ -1,14 +1,14 @@
 #!/usr/bin/env python3
 """Throughput of the MSA hot path on one MI355X.
 
-Default workload ("100M"): a 100M-token memory — 1,562,500 pooled chunks per
+Default workload ("100m"): a 100M-token memory — 1,562,500 pooled chunks per
 routed layer — with the router keys of all 18 routed layers resident in HBM
 (57.6 GB, bf16) and the pooled K̄/V̄ of one layer (6.4 GB) in pinned host
 memory, read by every layer; documents of 4–64 chunks; one planted needle per
 layer; one decode query (32 Q heads, 128 tokens of history + itself).
 
 One step = one decode query through all 18 layers, each layer running the
-whole hot path on the current stream:
+whole online path on the current stream:
     msa_route_scores  (cosine scan of the layer's 1,562,500 router keys)
     msa_select_topk   (chunk -> document max, top-16)
     msa_sparse_attend (chunk list, global RoPE, GQA attention over the
@@ -18,7 +18,14 @@ value = memory tokens routed per second per query = 18 × 100M / step time.
 
 The JSON line also carries the roofline of the dominant kernel (the routing
 scan: 2048 algorithmic bytes per chunk, timed with HIP events around its own
-launches in the timed region) and the CPU oracle timed on a bounded sample.
+launches inside the timed region) and the CPU oracle timed on a bounded sample.
+
+Other workloads (--workload) measure single stages for the design notes:
+  route16m    64 single-token queries against 250K pooled chunks (16M tokens):
+              batched MFMA routing + top-16
+  pool10m     Stage-1 pooling of 10M raw tokens (K, V, K^R, 61.4 GB read)
+  interleave  3 Memory-Interleave rounds (256 new tokens each) for 32 queries
+              over a pooled 10M-token memory
 """
 from __future__ import annotations
 
@@ -34,7 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-SCAN_BYTES_PER_CHUNK = 8 * 128 * 2          # one pooled router-key row
+ROW_BYTES = 8 * 128 * 2          # one pooled (or raw) row of one tensor: 8 heads × 128 bf16
 TOKENS_PER_CHUNK = 64
 
 
@@ -43,6 +50,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", choices=["100m", "route16m", "pool10m", "interleave"],
+                    default="100m")
     ap.add_argument("--layers", type=int, default=18)
     ap.add_argument("--chunks", type=int, default=1_562_500)
     ap.add_argument("--kv", choices=["host", "device"], default="host")
@@ -62,10 +71,10 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def stored_traffic(kernel_src):
-    """HBM bytes per scan launch measured with rocprofv3 counters (see
-    profiles/), valid only while the kernel source is unchanged."""
-    p = os.path.join(ROOT, "profiles", "traffic_route_scan.json")
+def stored_traffic(name, kernel_src):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/), used
+    only while the kernel source is unchanged since the measurement."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(p):
         return None
     t = json.load(open(p))
@@ -74,7 +83,65 @@ def stored_traffic(kernel_src):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(args, store, n_layers, dev_query, att0):
+def csrc(name):
+    return os.path.join(ROOT, "routed_sparse_attention_amd", "csrc", name)
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream every call uses)."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.spans = {}
+
+    def ev(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def add(self, key, a, b):
+        self.spans.setdefault(key, []).append((a, b))
+
+    def avg_us(self, key):
+        v = self.spans.get(key, [])
+        return sum(a.elapsed_time(b) for a, b in v) / max(1, len(v)) * 1e3
+
+
+def run_timed(args, step, timer):
+    """W untimed steps, then exactly K timed steps bracketed by synchronize."""
+    import torch
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step(timer)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / args.steps
+
+
+def base_result(args, metric, value, unit, ms, config):
+    return {
+        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config,
+    }
+
+
+def u16(t):
+    import numpy as np
+    import torch
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# default: 100M-token memory, 18 layers, one decode query
+# ---------------------------------------------------------------------------
+def cpu_baseline_100m(args, store, n_layers, query, att0):
     """The oracle, untouched, on a bounded sample of the same workload."""
     import numpy as np
     import torch
@@ -82,11 +149,10 @@ def cpu_baseline(args, store, n_layers, dev_query, att0):
 
     from oracle import msa_oracle as O
 
-    u16 = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
     C = store.n_chunks
     sample = min(args.cpu_sample_chunks, C)
     block = 100_000
-    qr = u16(dev_query.QR[0])
+    qr = u16(query.QR[0])
     with threadpool_limits(limits=1):
         t_route = 0.0
         done = 0
@@ -97,52 +163,40 @@ def cpu_baseline(args, store, n_layers, dev_query, att0):
             O.chunk_scores(qr, kr)
             t_route += time.perf_counter() - t0
             done += n
-        rng = np.random.default_rng(0)
-        S = rng.standard_normal(C)
+        S = np.random.default_rng(0).standard_normal(C)
         t0 = time.perf_counter()
         s = O.doc_scores(S, store.doc_chunk_offsets)
         O.topk(s, 16)
         t_select = time.perf_counter() - t0
         # a fixed selection (documents 0..15) gives the same amount of work
-        sel = list(range(16))
         dco = store.doc_chunk_offsets
-        rows = np.concatenate([np.arange(dco[i], dco[i + 1]) for i in sel])
+        rows = np.concatenate([np.arange(dco[i], dco[i + 1]) for i in range(16)])
         kbar = u16(store.Kbar[torch.from_numpy(rows)])
         vbar = u16(store.Vbar[torch.from_numpy(rows)])
-        sub_dco = np.concatenate([[0], np.cumsum([dco[i + 1] - dco[i] for i in sel])])
+        sub_dco = np.concatenate([[0], np.cumsum([dco[i + 1] - dco[i] for i in range(16)])])
         t0 = time.perf_counter()
         O.sparse_attend(u16(att0.Q), u16(att0.K_loc), u16(att0.V_loc), kbar, vbar, sub_dco,
                         list(range(16)))
         t_attend = time.perf_counter() - t0
     t_layer = t_route * (C / sample) + t_select + t_attend
-    value = n_layers * C * TOKENS_PER_CHUNK / (n_layers * t_layer)
     return {
-        "value": value, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "value": C * TOKENS_PER_CHUNK / t_layer, "unit": "tokens/s", "cores": 1, "kind": "oracle",
         "sample": (f"oracle routing over {sample:,} of {C:,} chunks of layer 0 "
                    f"({t_route:.2f} s, scaled to the full layer), document max + top-16 over "
                    f"{store.n_docs:,} documents ({t_select:.2f} s) and sparse attention for one "
-                   f"decode token over 16 documents ({t_attend:.2f} s); per-layer time × "
-                   f"{n_layers} layers; numpy fp64, 1 thread"),
+                   f"decode token over 16 documents ({t_attend:.2f} s); per-layer rate, equal "
+                   f"for {n_layers} layers; numpy fp64, 1 thread"),
         "seconds_measured": t_route + t_select + t_attend,
     }
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this MSA build measures one GPU; multi-GPU runs are not "
-                          "part of it (see the sharding notes in DESIGN.md)",
-                          "n_gpus": args.gpus}), flush=True)
-        sys.exit(2)
-
+def workload_100m(args):
     import numpy as np
     import torch
 
     import routed_sparse_attention_amd as msa
     import synth
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
     L = args.layers
     t_gen = time.perf_counter()
@@ -155,8 +209,7 @@ def main():
     C, N = store.n_chunks, store.n_docs
     d = msa.dims()
     dco = torch.from_numpy(store.doc_chunk_offsets).to(dev)
-    max_doc = int(np.diff(store.doc_chunk_offsets).max())
-    max_sel = d.top_k * max_doc
+    max_sel = d.top_k * int(np.diff(store.doc_chunk_offsets).max())
     QR = [q.QR for q in queries]
     S = torch.empty((1, C), dtype=torch.float32, device=dev)
     ds = torch.empty((1, N), dtype=torch.float32, device=dev)
@@ -170,98 +223,281 @@ def main():
     outs = [torch.empty((1, 32, 128), dtype=torch.bfloat16, device=dev) for _ in range(L)]
     Kb, Vb = store.Kbar, store.Vbar
 
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    timing = {"scan": [], "select": [], "attend": []}
-
-    def step(record):
+    def step(tm):
         for l in range(L):
-            e = [ev() for _ in range(4)] if record else None
-            if record:
-                e[0].record()
+            e0 = tm.ev() if tm else None
             msa.route_scores(QR[l], store.KRbar[l], d, out=S)
-            if record:
-                e[1].record()
+            e1 = tm.ev() if tm else None
             msa.select_topk(S, dco, d, doc_scores=ds, ws=ws_sel, outs=(ids, sc, ns))
-            if record:
-                e[2].record()
+            e2 = tm.ev() if tm else None
             msa.sparse_attend(atts[l].Q, atts[l].K_loc, atts[l].V_loc, Kb, Vb, dco, ids[0], ns,
                               max_sel, d=d, ws=ws_att, out=outs[l])
-            if record:
-                e[3].record()
-                timing["scan"].append((e[0], e[1]))
-                timing["select"].append((e[1], e[2]))
-                timing["attend"].append((e[2], e[3]))
+            if tm:
+                e3 = tm.ev()
+                tm.add("scan", e0, e1)
+                tm.add("select", e1, e2)
+                tm.add("attend", e2, e3)
 
     # correctness guard on the measured configuration: every layer's needle
-    step(False)
-    torch.cuda.synchronize()
     for l in range(L):
         msa.route_scores(QR[l], store.KRbar[l], d, out=S)
         msa.select_topk(S, dco, d, doc_scores=ds, ws=ws_sel, outs=(ids, sc, ns))
-        got = set(ids[0].cpu().tolist())
-        assert set(queries[l].planted_docs[0]) <= got, f"layer {l}: needle not selected"
+        assert set(queries[l].planted_docs[0]) <= set(ids[0].cpu().tolist()), \
+            f"layer {l}: needle not selected"
     log(args, "needles found in every layer")
 
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0, t1 = ev(), ev()
-    t0.record()
-    wall0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t0.elapsed_time(t1) / args.steps
-    avg = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) * 1e3 for k, v in timing.items()}  # µs
-
+    tm = Timer()
+    ms = run_timed(args, step, tm)
     tokens = C * TOKENS_PER_CHUNK
-    value = L * tokens / (ms_step * 1e-3)
-    scan_bytes = C * SCAN_BYTES_PER_CHUNK
-    achieved = scan_bytes / (avg["scan"] * 1e-6) / 1e9
-    traffic = stored_traffic(os.path.join(ROOT, "routed_sparse_attention_amd", "csrc",
-                                          "msa_route.hip"))
-    result = {
-        "metric": "memory tokens routed/sec per query",
-        "value": value,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": f"{tokens / 1e6:.0f}M-token memory, {L} routed layers, one decode query "
-                        f"per step",
-            "memory_tokens": tokens, "chunks_per_layer": C, "documents": N, "layers": L,
-            "top_k": d.top_k, "chunk": 64, "heads": 8, "head_dim": 128, "q_heads": 32,
-            "local_tokens": int(atts[0].K_loc.shape[0]),
-            "router_keys_bytes": L * scan_bytes,
-            "kv_tier": "pinned host (read in place over PCIe)" if args.kv == "host" else "HBM",
-        },
-        "route_scan_us_per_layer": avg["scan"],
-        "select_topk_us_per_layer": avg["select"],
-        "sparse_attend_us_per_query_layer": avg["attend"],
-        "route_tokens_per_s_per_layer": tokens / (avg["scan"] * 1e-6),
-        "roofline": {
-            "bound": "hbm", "kernel": "scan_valu_kernel (msa_route_scores)",
-            "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-            "bytes_per_launch": scan_bytes,
-        },
-        "wall_s_timed": wall,
-    }
+    scan_us = tm.avg_us("scan")
+    scan_bytes = C * ROW_BYTES
+    achieved = scan_bytes / (scan_us * 1e-6) / 1e9
+    r = base_result(args, "memory tokens routed/sec per query", L * tokens / (ms * 1e-3),
+                    "tokens/s", ms, {
+                        "workload": f"{tokens / 1e6:.0f}M-token memory, {L} routed layers, one "
+                                    f"decode query per step",
+                        "memory_tokens": tokens, "chunks_per_layer": C, "documents": N,
+                        "layers": L, "top_k": d.top_k, "chunk": 64, "heads": 8, "head_dim": 128,
+                        "q_heads": 32, "local_tokens": int(atts[0].K_loc.shape[0]),
+                        "router_keys_bytes": L * scan_bytes,
+                        "kv_tier": "pinned host (read in place over PCIe)" if args.kv == "host"
+                        else "HBM"})
+    r.update({
+        "route_scan_us_per_layer": scan_us,
+        "select_topk_us_per_layer": tm.avg_us("select"),
+        "sparse_attend_us_per_query_layer": tm.avg_us("attend"),
+        "route_tokens_per_s_per_layer": tokens / (scan_us * 1e-6),
+        "roofline": {"bound": "hbm", "kernel": "scan_valu_kernel<1> (msa_route_scores)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": stored_traffic("route_scan", csrc("msa_route.hip")),
+                     "bytes_per_launch": scan_bytes},
+    })
     if not args.no_cpu_baseline:
         log(args, "timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(args, store, L, queries[0], atts[0])
+        r["cpu_baseline"] = cpu_baseline_100m(args, store, L, queries[0], atts[0])
     else:
-        result["cpu_baseline"] = None
-    print(json.dumps(result), flush=True)
+        r["cpu_baseline"] = None
+    return r
+
+
+# ---------------------------------------------------------------------------
+# route16m: 64 single-token queries, 250K chunks (batched MFMA routing)
+# ---------------------------------------------------------------------------
+def workload_route16m(args):
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import routed_sparse_attention_amd as msa
+    import synth
+
+    dev = "cuda"
+    store, q = synth.cfg3_batched(dev)
+    B, C, N = q.QR.shape[0], store.n_chunks, store.n_docs
+    d = msa.dims()
+    dco = torch.from_numpy(store.doc_chunk_offsets).to(dev)
+    S = torch.empty((B, C), dtype=torch.float32, device=dev)
+    ds = torch.empty((B, N), dtype=torch.float32, device=dev)
+    outs = (torch.empty((B, 16), dtype=torch.int32, device=dev),
+            torch.empty((B, 16), dtype=torch.float32, device=dev),
+            torch.empty((B,), dtype=torch.int32, device=dev))
+    msa.route_scores(q.QR, store.KRbar, d, out=S)
+    msa.select_topk(S, dco, d, doc_scores=ds, outs=outs)
+    ids = outs[0].cpu().numpy()
+    for b in range(B):
+        assert set(q.planted_docs[b]) <= set(ids[b].tolist()), f"query {b}: planted doc missed"
+
+    def step(tm):
+        e0 = tm.ev() if tm else None
+        msa.route_scores(q.QR, store.KRbar, d, out=S)
+        e1 = tm.ev() if tm else None
+        msa.select_topk(S, dco, d, doc_scores=ds, outs=outs)
+        if tm:
+            e2 = tm.ev()
+            tm.add("scan", e0, e1)
+            tm.add("select", e1, e2)
+
+    tm = Timer()
+    ms = run_timed(args, step, tm)
+    tokens = C * TOKENS_PER_CHUNK
+    scan_us = tm.avg_us("scan")
+    achieved = C * ROW_BYTES / (scan_us * 1e-6) / 1e9
+    r = base_result(args, "memory tokens routed/sec per query", tokens / (ms * 1e-3), "tokens/s",
+                    ms, {"workload": f"{tokens / 1e6:.0f}M-token memory, {B} single-token "
+                                     f"queries routed together (top-16 each)",
+                         "memory_tokens": tokens, "chunks": C, "documents": N, "queries": B})
+    r.update({
+        "aggregate_tokens_per_s": B * tokens / (ms * 1e-3),
+        "route_scan_us": scan_us, "select_topk_us": tm.avg_us("select"),
+        "roofline": {"bound": "hbm", "kernel": "scan_mfma_kernel (msa_route_scores)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": stored_traffic("route_mfma", csrc("msa_route_mfma.hip")),
+                     "bytes_per_launch": C * ROW_BYTES,
+                     "algorithmic_tflops": 2.0 * B * C * 1024 / (scan_us * 1e-6) / 1e12},
+    })
+    if not args.no_cpu_baseline:
+        from oracle import msa_oracle as O
+        sample = 20_000
+        kr = u16(store.KRbar[:sample])
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            for b in range(B):
+                O.chunk_scores(u16(q.QR[b]), kr)
+            t = time.perf_counter() - t0
+        r["cpu_baseline"] = {"value": tokens / (t * C / sample), "unit": "tokens/s", "cores": 1,
+                             "kind": "oracle",
+                             "sample": f"oracle routing of all {B} queries over {sample:,} of "
+                                       f"{C:,} chunks ({t:.2f} s), scaled to the full store; "
+                                       f"numpy fp64, 1 thread"}
+    else:
+        r["cpu_baseline"] = None
+    return r
+
+
+# ---------------------------------------------------------------------------
+# pool10m: Stage-1 pooling of 10M raw tokens
+# ---------------------------------------------------------------------------
+def workload_pool10m(args):
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import routed_sparse_attention_amd as msa
+    import synth
+
+    dev = "cuda"
+    t_gen = time.perf_counter()
+    mem, _ = synth.cfg5_memory(dev)
+    torch.cuda.synchronize()
+    log(args, f"generated 10M raw tokens in {time.perf_counter() - t_gen:.1f} s")
+    d = msa.dims()
+    dco_h = msa.plan_chunks(mem.doc_token_offsets)
+    C = int(dco_h[-1])
+    T = mem.n_tokens
+    dto = torch.from_numpy(mem.doc_token_offsets).to(dev)
+    dco = torch.from_numpy(dco_h).to(dev)
+    out = tuple(torch.empty((C, 8, 128), dtype=torch.bfloat16, device=dev) for _ in range(3))
+
+    def step(tm):
+        e0 = tm.ev() if tm else None
+        msa.encode_pool(mem.K, mem.V, mem.KR, dto, dco, C, d, out=out)
+        if tm:
+            tm.add("pool", e0, tm.ev())
+
+    tm = Timer()
+    ms = run_timed(args, step, tm)
+    pool_us = tm.avg_us("pool")
+    nbytes = 3 * ROW_BYTES * (T + C)
+    achieved = nbytes / (pool_us * 1e-6) / 1e9
+    r = base_result(args, "memory tokens encoded/sec", T / (ms * 1e-3), "tokens/s", ms,
+                    {"workload": f"Stage-1 pooling of {T / 1e6:.0f}M raw tokens "
+                                 f"({mem.n_docs:,} documents of 256-8192 tokens)",
+                     "tokens": T, "chunks": C, "documents": mem.n_docs})
+    r.update({
+        "pool_us": pool_us,
+        "roofline": {"bound": "hbm", "kernel": "pool_kernel (msa_encode_pool)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": stored_traffic("pool", csrc("msa_pool.hip")),
+                     "bytes_per_launch": nbytes},
+    })
+    if not args.no_cpu_baseline:
+        from oracle import msa_oracle as O
+        offs = mem.doc_token_offsets
+        docs, tok = [], 0
+        for i in range(mem.n_docs):
+            docs.append(i)
+            tok += int(offs[i + 1] - offs[i])
+            if tok >= 200_000:
+                break
+        t_end = int(offs[docs[-1] + 1])
+        K, V, R = u16(mem.K[:t_end]), u16(mem.V[:t_end]), u16(mem.KR[:t_end])
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            O.pool(K, V, R, offs[:docs[-1] + 2], docs=docs)
+            t = time.perf_counter() - t0
+        r["cpu_baseline"] = {"value": tok / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                             "sample": f"oracle pooling of the first {len(docs)} documents "
+                                       f"({tok:,} tokens, {t:.2f} s); numpy fp64, 1 thread"}
+    else:
+        r["cpu_baseline"] = None
+    return r
+
+
+# ---------------------------------------------------------------------------
+# interleave: 32 queries × 3 rounds over a pooled 10M-token memory
+# ---------------------------------------------------------------------------
+def workload_interleave(args):
+    import numpy as np
+    import torch
+
+    import routed_sparse_attention_amd as msa
+    import synth
+
+    dev = "cuda"
+    mem, chains = synth.cfg5_memory(dev)
+    d = msa.dims()
+    dco_h = msa.plan_chunks(mem.doc_token_offsets)
+    C = int(dco_h[-1])
+    dto = torch.from_numpy(mem.doc_token_offsets).to(dev)
+    dco = torch.from_numpy(dco_h).to(dev)
+    Kb, Vb, Rb = msa.encode_pool(mem.K, mem.V, mem.KR, dto, dco, C, d)
+    torch.cuda.synchronize()
+    rounds = [[synth.cfg5_round(mem, doc, qi, r, device=dev) for r, doc in enumerate(ch)]
+              for qi, ch in enumerate(chains)]
+    mem.K = mem.V = mem.KR = None
+    max_sel = d.top_k * int(np.diff(dco_h).max())
+    n_q, n_r = len(chains), len(chains[0])
+    n_docs = len(dco_h) - 1
+    states = [msa.Interleave(n_docs, cap_loc=n_r * 256, d=d) for _ in range(n_q)]
+    need = msa.lib().msa_interleave_step_workspace(ctypes.byref(d), 256, n_r * 256, C, n_docs,
+                                                   max_sel)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.empty((256, 32, 128), dtype=torch.bfloat16, device=dev)
+
+    def one_pass(tm):
+        for qi in range(n_q):
+            st = states[qi]
+            st.reset()
+            for r in range(n_r):
+                QR, Q, Kn, Vn = rounds[qi][r]
+                e0 = tm.ev() if tm else None
+                st.step(Q, Kn, Vn, QR, Rb, Kb, Vb, dco, max_sel, ws=ws, out=out)
+                if tm:
+                    tm.add("round", e0, tm.ev())
+
+    one_pass(None)
+    torch.cuda.synchronize()
+    found = sum(int(all(doc in set(states[qi].topk_ids.cpu().tolist()) for doc in chains[qi]))
+                for qi in range(n_q))
+    tm = Timer()
+    ms = run_timed(args, one_pass, tm)
+    tokens = C * TOKENS_PER_CHUNK
+    routed = n_q * n_r * tokens
+    r = base_result(args, "memory tokens routed/sec per query", routed / (ms * 1e-3), "tokens/s",
+                    ms, {"workload": f"Memory Interleave: {n_q} queries × {n_r} rounds of 256 "
+                                     f"new tokens over a {tokens / 1e6:.1f}M-token pooled memory",
+                         "queries": n_q, "rounds": n_r, "new_tokens_per_round": 256,
+                         "memory_tokens": tokens, "chunks": C})
+    r.update({"round_us": tm.avg_us("round"),
+              "queries_with_whole_chain_selected": f"{found}/{n_q}",
+              "roofline": None, "cpu_baseline": None})
+    return r
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this MSA build measures one GPU; multi-GPU runs are not "
+                          "part of it (see the sharding notes in DESIGN.md)",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    fn = {"100m": workload_100m, "route16m": workload_route16m, "pool10m": workload_pool10m,
+          "interleave": workload_interleave}[args.workload]
+    print(json.dumps(fn(args)), flush=True)
 
 
 if __name__ == "__main__":

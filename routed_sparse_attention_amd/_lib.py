@@ -306,7 +306,11 @@ class Interleave:
         self.n_sel = torch.empty((1,), dtype=torch.int32, device=device)
         self.st = InterleaveStateC(_p(self.doc_scores), _p(self.K_loc), _p(self.V_loc), cap_loc, 0,
                                    _p(self.topk_ids), _p(self.topk_scores), _p(self.n_sel), pos0)
-        _check(lib().msa_interleave_reset(ctypes.byref(self.st), n_docs, _stream()))
+        self.reset()
+
+    def reset(self):
+        """Forget every round: running scores to -inf, no local tokens."""
+        _check(lib().msa_interleave_reset(ctypes.byref(self.st), self.n_docs, _stream()))
 
     @property
     def n_loc(self) -> int:

@@ -80,7 +80,7 @@ int resolve_kv(const void* p, int on_host, const void** out, const char* name) {
 
 // Scan plan: kernel choice (VALU for <= 8 query rows, MFMA above) and the
 // partials buffer needed when a query's tokens span several row tiles.
-constexpr bool kHaveMfmaScan = false;
+constexpr bool kHaveMfmaScan = true;
 
 struct ScanPlan {
   bool mfma;

@@ -314,46 +314,37 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
                                                       int32_t n_splits, int64_t n_rows,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ out_f32) {
-  __shared__ float w[kMaxSplits];
-  __shared__ float s_mx, s_L;
+  __shared__ float ms[kMaxSplits], ls[kMaxSplits];
   const int64_t row = blockIdx.x;
   const int d = threadIdx.x;
-  for (int s = d; s < n_splits; s += blockDim.x) w[s] = ML[((int64_t)s * n_rows + row) * 2];
-  __syncthreads();
-  if (d == 0) {
-    float mx = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, w[s]);
-    s_mx = mx;
-  }
-  __syncthreads();
-  const float mx = s_mx;
   for (int s = d; s < n_splits; s += blockDim.x) {
-    const float m = w[s];
-    w[s] = (mx == -INFINITY || m == -INFINITY) ? 0.0f : exp2f(m - mx);
+    ms[s] = ML[((int64_t)s * n_rows + row) * 2];
+    ls[s] = ML[((int64_t)s * n_rows + row) * 2 + 1];
   }
   __syncthreads();
-  if (d == 0) {
-    float L = 0.0f;
-    for (int s = 0; s < n_splits; ++s)
-      if (w[s] != 0.0f) L += w[s] * ML[((int64_t)s * n_rows + row) * 2 + 1];
-    s_L = L;
-  }
-  float acc = 0.0f;
-  for (int s0 = 0; s0 < n_splits; s0 += 8) {
-    float x[8];
+  float mx = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, ms[s]);
+  float L = 0.0f, acc = 0.0f;
+  if (mx != -INFINITY) {
+    for (int s0 = 0; s0 < n_splits; s0 += 8) {
+      float x[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = s0 + u;
-      x[u] = (s < n_splits && w[s] != 0.0f) ? Opart[((int64_t)s * n_rows + row) * kDim + d] : 0.0f;
-    }
+      for (int u = 0; u < 8; ++u) {
+        const int s = s0 + u;
+        x[u] = (s < n_splits && ms[s] != -INFINITY) ? Opart[((int64_t)s * n_rows + row) * kDim + d]
+                                                    : 0.0f;
+      }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = s0 + u;
-      if (s < n_splits) acc += w[s] * x[u];
+      for (int u = 0; u < 8; ++u) {
+        const int s = s0 + u;
+        if (s < n_splits && ms[s] != -INFINITY) {
+          const float w = exp2f(ms[s] - mx);
+          L += w * ls[s];
+          acc += w * x[u];
+        }
+      }
     }
   }
-  __syncthreads();
-  const float L = s_L;
   const float o = L > 0.0f ? acc / L : 0.0f;
   out[row * kDim + d] = f2bf(o);
   if (out_f32) out_f32[row * kDim + d] = o;

@@ -8,19 +8,19 @@
 //
 // Design.
 //   doc_max: one thread per (document, query); each thread reads its chunk
-//     range with 8 independent loads in flight and max-reduces it (NaN
+//     range with 16 independent loads in flight and max-reduces it (NaN
 //     propagates, as numpy's max does), max-merges with the previous score
 //     when accumulating, and writes the document score.
 //   topk_select: one 1024-thread workgroup per query. Each document becomes
 //     the unique 64-bit key (order-preserving uint32 of the score) << 32 |
 //     (0xFFFFFFFF − id), so larger key = better document and equal scores
 //     fall back to the lower id (NaN maps to the lowest scores).
-//     Fast path (k <= 16): every wave takes the maximum key of its share;
-//     the smallest of the 16 wave maxima is a lower bound on the k-th best
-//     key (16 distinct keys reach it), so only keys at or above it — a few
-//     dozen on real data — are appended (ballot-compacted) to an LDS list,
-//     which is bitonic-sorted; its head is the answer.
-//     Fallback (more than 2048 candidates, i.e. massive ties, or k > 16):
+//     Fast path: doc_max also writes the best key of every block of 256
+//     documents. T = the k-th best block maximum is reached by at least k
+//     documents, and only blocks whose maximum reaches T (about k of them)
+//     can hold a key >= T; those keys are ballot-compacted into LDS and
+//     bitonic-sorted, and the head of the list is the answer.
+//     Fallback (massive ties at T, or more than 2048 blocks):
 //     radix select on the uint32 score keys. Four passes
 //     over 8-bit digits, most significant first, histogram the keys that
 //     share the digits fixed so far (one LDS histogram per wave, rows padded
@@ -41,30 +41,59 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kHistPitch = 257;
 constexpr int kMaxK = 64;
 constexpr int kCandCap = 2048;
+constexpr int kMaxHot = 512;
+
+__device__ __forceinline__ uint64_t doc_key(float score, int64_t i) {
+  return ((uint64_t)ord_key(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
 
 __global__ __launch_bounds__(256) void doc_max_kernel(const float* __restrict__ S, int64_t C,
                                                       const int64_t* __restrict__ dco,
                                                       int32_t n_docs,
                                                       float* __restrict__ doc_scores,
-                                                      int32_t accumulate) {
+                                                      int32_t accumulate,
+                                                      uint64_t* __restrict__ bmax) {
+  __shared__ uint64_t wbest[kMaxThreads / 64];
   const int b = blockIdx.y;
   const int64_t i = (int64_t)blockIdx.x * kMaxThreads + threadIdx.x;
-  if (i >= n_docs) return;
-  int64_t c0 = dco[i], c1 = dco[i + 1];
-  c0 = max((int64_t)0, min(c0, C));
-  c1 = max(c0, min(c1, C));
-  const float* Sb = S + (int64_t)b * C;
-  float s = -INFINITY;
-  for (int64_t c = c0; c < c1; c += 8) {
-    float v[8];
+  uint64_t key = 0;
+  if (i < n_docs) {
+    int64_t c0 = dco[i], c1 = dco[i + 1];
+    c0 = max((int64_t)0, min(c0, C));
+    c1 = max(c0, min(c1, C));
+    const float* Sb = S + (int64_t)b * C;
+    float s = -INFINITY;
+    for (int64_t c = c0; c < c1; c += 16) {
+      float v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = (c + u < c1) ? Sb[c + u] : -INFINITY;
+      for (int u = 0; u < 16; ++u) v[u] = (c + u < c1) ? Sb[c + u] : -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s = nan_max(s, v[u]);
+      for (int u = 0; u < 16; ++u) s = nan_max(s, v[u]);
+    }
+    float* ds = doc_scores + (int64_t)b * n_docs + i;
+    if (accumulate) s = nan_max(*ds, s);
+    *ds = s;
+    key = doc_key(s, i);
   }
-  float* ds = doc_scores + (int64_t)b * n_docs + i;
-  if (accumulate) s = nan_max(*ds, s);
-  *ds = s;
+  // the best document key of this block of 256 documents
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t y = shfl_xor_u64(key, o);
+    key = y > key ? y : key;
+  }
+  if ((threadIdx.x & 63) == 0) wbest[threadIdx.x >> 6] = key;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t best = 0;
+    for (int w = 0; w < kMaxThreads / 64; ++w) best = wbest[w] > best ? wbest[w] : best;
+    bmax[(int64_t)b * gridDim.x + blockIdx.x] = best;
+  }
 }
 
 // Radix-select fallback: fills sel[0..Ks) with the Ks best 64-bit keys (any
@@ -151,85 +180,102 @@ __device__ void radix_select(const float* __restrict__ s, int N, int Ks, uint32_
   __syncthreads();
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, m);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t doc_key(float score, int i) {
-  return ((uint64_t)ord_key(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+// Bitonic sort of n2 (a power of two, <= kCandCap) keys in LDS, descending.
+__device__ void bitonic_desc(uint64_t* a, int n2) {
+  const int tid = threadIdx.x;
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int p = tid; p < n2 / 2; p += kSelThreads) {
+        const int i = 2 * j * (p / j) + (p % j);
+        const int l = i + j;
+        const bool desc = (i & k) == 0;
+        const uint64_t x = a[i], y = a[l];
+        if (desc ? (x < y) : (x > y)) { a[i] = y; a[l] = x; }
+      }
+      __syncthreads();
+    }
+  }
 }
 
 __global__ __launch_bounds__(1024) void topk_select_kernel(const float* __restrict__ doc_scores,
-                                                           int32_t N, int32_t K,
+                                                           const uint64_t* __restrict__ bmax,
+                                                           int32_t n_blocks, int32_t N,
+                                                           int32_t K,
                                                            int32_t* __restrict__ topk_ids,
                                                            float* __restrict__ topk_scores,
                                                            int32_t* __restrict__ n_sel) {
   __shared__ uint64_t cand[kCandCap];
-  __shared__ uint64_t wmax[kSelWaves];
   __shared__ uint32_t hist[kSelWaves * kHistPitch];
   __shared__ uint32_t tot[256];
   __shared__ uint32_t wave_eq[kSelWaves];
   __shared__ uint32_t scratch[4];
+  __shared__ int hot[kMaxHot];
   __shared__ int n_cand;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int b = blockIdx.x;
   const float* s = doc_scores + (int64_t)b * N;
+  const uint64_t* bm = bmax + (int64_t)b * n_blocks;
   const int Ks = N < K ? N : K;
 
   int cnt = kCandCap + 1;  // forces the fallback unless the fast path applies
-  if (K <= kSelWaves) {
-    uint64_t best = 0;
-    for (int i = tid; i < N; i += kSelThreads) {
-      const uint64_t k = doc_key(s[i], i);
-      best = k > best ? k : best;
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint64_t y = shfl_xor_u64(best, o);
-      best = y > best ? y : best;
-    }
-    if (lane == 0) wmax[wave] = best;
+  if (n_blocks >= K && n_blocks <= kCandCap) {
+    // ---- T = K-th best block maximum: at least K documents reach it, and a
+    //      document at or above T can only sit in a block whose maximum does
+    int n2 = 1;
+    while (n2 < n_blocks) n2 <<= 1;
+    for (int i = tid; i < n2; i += kSelThreads) cand[i] = i < n_blocks ? bm[i] : 0ull;
     if (tid == 0) n_cand = 0;
     __syncthreads();
-    uint64_t T = ~0ull;
-    for (int w = 0; w < kSelWaves; ++w) T = wmax[w] < T ? wmax[w] : T;  // 0 if a wave had no keys
-    for (int i = tid; i < N; i += kSelThreads) {
-      const uint64_t k = doc_key(s[i], i);
-      const bool c = k >= T;
-      const uint64_t m = __ballot(c);
-      if (m) {
-        int base = 0;
-        if (lane == 0) base = atomicAdd(&n_cand, (int)__popcll(m));
-        base = __shfl(base, 0);
-        const int pos = base + (int)__popcll(m & ((1ull << lane) - 1ull));
-        if (c && pos < kCandCap) cand[pos] = k;
+    bitonic_desc(cand, n2);
+    const uint64_t T = cand[K - 1];
+    int n_hot = 0;  // blocks whose maximum reaches T (a prefix of the sorted list)
+    for (int i = 0; i < n_blocks && cand[i] >= T; ++i) ++n_hot;
+    // block ids of the hot blocks, from their maximum's document id
+    int hot_blk = -1;
+    if (tid < n_hot) hot_blk = (int)((0xFFFFFFFFu - (uint32_t)(cand[tid] & 0xFFFFFFFFu)) / kMaxThreads);
+    // ---- gather keys >= T from the hot blocks (256 documents each)
+    if (n_hot <= kMaxHot) {
+      if (tid < n_hot) hot[tid] = hot_blk;
+      __syncthreads();
+      const int total = n_hot * kMaxThreads;
+      for (int base = 0; base < total; base += kSelThreads) {
+        const int j = base + tid;
+        uint64_t k = 0;
+        bool c = false;
+        if (j < total) {
+          const int64_t i = (int64_t)hot[j / kMaxThreads] * kMaxThreads + (j % kMaxThreads);
+          if (i < N) {
+            k = doc_key(s[i], i);
+            c = k >= T;
+          }
+        }
+        const uint64_t m = __ballot(c);
+        if (m) {
+          int pos0 = 0;
+          if (lane == 0) pos0 = atomicAdd(&n_cand, (int)__popcll(m));
+          pos0 = __shfl(pos0, 0);
+          const int pos = pos0 + (int)__popcll(m & ((1ull << lane) - 1ull));
+          if (c && pos < kCandCap) cand[pos] = k;
+        }
       }
+      __syncthreads();
+      cnt = n_cand;
     }
+  } else if (N <= kCandCap) {
+    for (int i = tid; i < N; i += kSelThreads) cand[i] = doc_key(s[i], i);
+    cnt = N;
     __syncthreads();
-    cnt = n_cand;
   }
   if (cnt <= kCandCap) {
     int n2 = 1;
     while (n2 < cnt) n2 <<= 1;
     for (int i = cnt + tid; i < n2; i += kSelThreads) cand[i] = 0;
     __syncthreads();
-    for (int k = 2; k <= n2; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int p = tid; p < n2 / 2; p += kSelThreads) {
-          const int i = 2 * j * (p / j) + (p % j);
-          const int l = i + j;
-          const bool desc = (i & k) == 0;
-          const uint64_t x = cand[i], y = cand[l];
-          if (desc ? (x < y) : (x > y)) { cand[i] = y; cand[l] = x; }
-        }
-        __syncthreads();
-      }
-    }
+    bitonic_desc(cand, n2);
   } else {
-    // massive ties or k > 16: radix select into cand[0..Ks), then rank
+    // massive ties at the threshold (or an unusual shape): radix select into
+    // cand[kMaxK..), then rank into cand[0..Ks)
     radix_select(s, N, Ks, hist, tot, wave_eq, cand + kMaxK, &n_cand, scratch);
     if (tid < Ks) {
       const uint64_t e = cand[kMaxK + tid];
@@ -263,22 +309,22 @@ __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
 }  // namespace
 
 size_t doc_topk_workspace(int32_t B, int32_t n_docs, int32_t top_k) {
-  (void)B; (void)n_docs; (void)top_k;
-  return 0;
+  (void)top_k;
+  const int64_t n_blocks = (n_docs + kMaxThreads - 1) / kMaxThreads;
+  return align_up((size_t)B * n_blocks * sizeof(uint64_t), 256);
 }
 
 int launch_doc_topk(const float* S, int32_t B, int64_t n_chunks, const int64_t* dco,
                     int32_t n_docs, float* doc_scores, int32_t accumulate, int32_t top_k,
                     uint64_t* cand, int32_t* topk_ids, float* topk_scores, int32_t* n_sel,
                     hipStream_t s) {
-  (void)cand;
   if (top_k > kMaxK) return fail(MSA_ERR_UNSUPPORTED, "top_k > %d", kMaxK);
   const unsigned blocks = (unsigned)((n_docs + kMaxThreads - 1) / kMaxThreads);
   hipLaunchKernelGGL(doc_max_kernel, dim3(blocks, B), dim3(kMaxThreads), 0, s, S, n_chunks, dco,
-                     n_docs, doc_scores, accumulate);
+                     n_docs, doc_scores, accumulate, cand);
   MSA_LAUNCH_CHECK("doc_max_kernel launch");
-  hipLaunchKernelGGL(topk_select_kernel, dim3(B), dim3(kSelThreads), 0, s, doc_scores, n_docs,
-                     top_k, topk_ids, topk_scores, n_sel);
+  hipLaunchKernelGGL(topk_select_kernel, dim3(B), dim3(kSelThreads), 0, s, doc_scores, cand,
+                     (int32_t)blocks, n_docs, top_k, topk_ids, topk_scores, n_sel);
   MSA_LAUNCH_CHECK("topk_select_kernel launch");
   return MSA_OK;
 }

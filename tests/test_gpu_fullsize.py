@@ -1,0 +1,206 @@
+"""Parity at the full workload sizes, in the launch configurations bench.py
+times. The oracle cannot redo every output at these sizes, so each test
+recomputes a sample one by one (whole layers where that fits in seconds) and
+checks properties that hold at any size:
+
+  - "1M" (1500 docs, 3.26M tokens): pooling of sampled documents, full routing
+    of the 128-token query (every document score) and the top-16 rule,
+    sparse attention over a test-chosen selection;
+  - "16M" (250K chunks, 64 single-token queries, batched MFMA scan): document
+    scores of sampled documents per query, top-16 validity against the GPU's
+    own scores, planted-document recall;
+  - "100M" (18 layers × 1,562,500 chunks, pinned-host K̄/V̄): every document
+    score of layer 0, the top-16 rule, needle recall in all 18 layers, decode
+    attention over a test-chosen selection read from pinned host memory;
+  - "10M encode + interleave": pooling of sampled documents (first, last,
+    partial chunks) and three interleave rounds (chain recall, routing sample).
+"""
+import numpy as np
+import pytest
+import torch
+
+import routed_sparse_attention_amd as msa
+import synth
+from oracle import msa_oracle as O
+from tests._util import (assert_attn_close, assert_pooled_close, assert_scores_close,
+                         assert_topk_matches, u16)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _banner(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _free():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _topk_valid_on_gpu_scores(ds, ids, ns, k):
+    """Selected ids are the k best of the GPU's own document scores."""
+    ds = np.asarray(ds, dtype=np.float64)
+    n = int(ns)
+    sel = ids[:n]
+    assert n == min(k, len(ds)) and len(set(sel.tolist())) == n
+    order = sorted(range(len(ds)), key=lambda i: (-ds[i], i))
+    assert list(sel) == order[:n]
+
+
+def _sample_docs(rng, n_docs, extra, n=40):
+    pick = set(int(x) for x in rng.choice(n_docs, size=min(n, n_docs), replace=False))
+    pick |= {0, n_docs - 1} | set(int(x) for x in extra)
+    return sorted(pick)
+
+
+def _doc_scores_oracle(QR_bits, KR_dev, dco_h, docs):
+    out = []
+    for i in docs:
+        kr = u16(KR_dev[int(dco_h[i]):int(dco_h[i + 1])])
+        out.append(O.chunk_scores(QR_bits, kr).max())
+    return np.array(out)
+
+
+def test_fullsize_1m():
+    _banner("full size: 1500 docs, 3.26M tokens, 128-token query")
+    mem, q, att = synth.cfg2_1m(DEV)
+    dco_h = msa.plan_chunks(mem.doc_token_offsets)
+    C, N = int(dco_h[-1]), mem.n_docs
+    dto = torch.from_numpy(mem.doc_token_offsets).to(DEV)
+    dco = torch.from_numpy(dco_h).to(DEV)
+    Kb, Vb, Rb = msa.encode_pool(mem.K, mem.V, mem.KR, dto, dco, C)
+    ds, ids, sc, ns = msa.route_topk(q.QR, Rb, dco)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(101)
+    # pooling: sampled documents, all three tensors
+    docs = _sample_docs(rng, N, list(mem.planted), 12)
+    offs = mem.doc_token_offsets
+    for i in docs:
+        t0, t1 = int(offs[i]), int(offs[i + 1])
+        oK, oV, oR, sub = O.pool(u16(mem.K[t0:t1]), u16(mem.V[t0:t1]), u16(mem.KR[t0:t1]),
+                                 np.array([0, t1 - t0]))
+        r0, r1 = int(dco_h[i]), int(dco_h[i + 1])
+        for g, e, n in ((Kb, oK, "K"), (Vb, oV, "V"), (Rb, oR, "KR")):
+            assert_pooled_close(u16(g[r0:r1]), e, f"doc {i} {n}")
+    # routing: every document score, and the top-16 rule
+    Rb_bits = u16(Rb)
+    s = O.doc_scores(O.chunk_scores(u16(q.QR[0]), Rb_bits), dco_h)
+    assert_scores_close(ds.cpu().numpy()[0], s, "doc scores")
+    assert_topk_matches(ids.cpu().numpy()[0], ns.cpu().numpy()[0], s, 16)
+    assert q.planted_docs[0][0] in set(ids.cpu().numpy()[0].tolist())
+    # attention: a test-chosen selection (the needle and 15 seeded documents)
+    needle = q.planted_docs[0][0]
+    sel = [needle] + [int(x) for x in rng.permutation(N) if int(x) != needle][:15]
+    assert len(sel) == 16 and len(set(sel)) == 16
+    sel_t = torch.tensor(sel, dtype=torch.int32, device=DEV)
+    ns_t = torch.tensor([16], dtype=torch.int32, device=DEV)
+    max_sel = 16 * int(np.diff(dco_h).max())
+    out, of = msa.sparse_attend(att.Q, att.K_loc, att.V_loc, Kb, Vb, dco, sel_t, ns_t, max_sel,
+                                want_f32=True)
+    torch.cuda.synchronize()
+    ref = O.sparse_attend(u16(att.Q), u16(att.K_loc), u16(att.V_loc), u16(Kb), u16(Vb), dco_h, sel)
+    assert_attn_close(of.cpu().numpy(), ref, "attention")
+
+
+def test_fullsize_16m_batched():
+    _banner("full size: 250K chunks, 64 single-token queries (MFMA scan)")
+    store, q = synth.cfg3_batched(DEV)
+    dco_h = store.doc_chunk_offsets
+    dco = torch.from_numpy(dco_h).to(DEV)
+    ds, ids, sc, ns = msa.route_topk(q.QR, store.KRbar, dco)
+    torch.cuda.synchronize()
+    ds, ids, ns = ds.cpu().numpy(), ids.cpu().numpy(), ns.cpu().numpy()
+    rng = np.random.default_rng(102)
+    for b in range(q.QR.shape[0]):
+        _topk_valid_on_gpu_scores(ds[b], ids[b], ns[b], 16)
+        assert set(q.planted_docs[b]) <= set(ids[b].tolist()), f"query {b}: planted doc missed"
+        if b % 8 == 0:
+            docs = _sample_docs(rng, store.n_docs, list(ids[b][:16]) + q.planted_docs[b], 24)
+            exp = _doc_scores_oracle(u16(q.QR[b]), store.KRbar, dco_h, docs)
+            assert_scores_close(ds[b][docs], exp, f"query {b} sampled doc scores")
+
+
+def test_fullsize_100m_layers():
+    _banner("full size: 18 layers × 1,562,500 chunks, pinned-host K/V")
+    store, queries, atts = synth.cfg4_100m(DEV, kv_pinned=True)
+    dco_h = store.doc_chunk_offsets
+    dco = torch.from_numpy(dco_h).to(DEV)
+    d = msa.dims()
+    C, N = store.n_chunks, store.n_docs
+    S = torch.empty((1, C), dtype=torch.float32, device=DEV)
+    for l in range(store.KRbar.shape[0]):
+        msa.route_scores(queries[l].QR, store.KRbar[l], d, out=S)
+        ds, ids, sc, ns = msa.select_topk(S, dco, d)
+        torch.cuda.synchronize()
+        ids_h = ids.cpu().numpy()[0]
+        assert set(queries[l].planted_docs[0]) <= set(ids_h.tolist()), f"layer {l}: needle"
+        _topk_valid_on_gpu_scores(ds.cpu().numpy()[0], ids_h, ns.cpu().numpy()[0], 16)
+        if l == 0:
+            # every document score of layer 0, in blocks of the store
+            qr = u16(queries[0].QR[0])
+            Sc = np.empty(C)
+            for c0 in range(0, C, 200_000):
+                c1 = min(C, c0 + 200_000)
+                Sc[c0:c1] = O.chunk_scores(qr, u16(store.KRbar[0, c0:c1]))
+            s = O.doc_scores(Sc, dco_h)
+            assert_scores_close(ds.cpu().numpy()[0], s, "layer 0 doc scores")
+            assert_topk_matches(ids_h, ns.cpu().numpy()[0], s, 16)
+    # decode attention in the bench configuration: K̄/V̄ read from pinned host memory
+    rng = np.random.default_rng(103)
+    sel = [int(x) for x in rng.choice(N, 16, replace=False)]
+    sel_t = torch.tensor(sel, dtype=torch.int32, device=DEV)
+    ns_t = torch.tensor([16], dtype=torch.int32, device=DEV)
+    max_sel = 16 * int(np.diff(dco_h).max())
+    att = atts[0]
+    out, of = msa.sparse_attend(att.Q, att.K_loc, att.V_loc, store.Kbar, store.Vbar, dco, sel_t,
+                                ns_t, max_sel, want_f32=True)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(dco_h[i], dco_h[i + 1]) for i in sel])
+    sub_dco = np.concatenate([[0], np.cumsum([dco_h[i + 1] - dco_h[i] for i in sel])])
+    kb = u16(store.Kbar[torch.from_numpy(rows)])
+    vb = u16(store.Vbar[torch.from_numpy(rows)])
+    ref = O.sparse_attend(u16(att.Q), u16(att.K_loc), u16(att.V_loc), kb, vb, sub_dco,
+                          list(range(16)))
+    assert_attn_close(of.cpu().numpy(), ref, "decode attention")
+
+
+def test_fullsize_10m_encode_and_interleave():
+    _banner("full size: 10M raw tokens pooled, 3 interleave rounds")
+    mem, chains = synth.cfg5_memory(DEV)
+    d = msa.dims()
+    dco_h = msa.plan_chunks(mem.doc_token_offsets)
+    C, N = int(dco_h[-1]), mem.n_docs
+    dto = torch.from_numpy(mem.doc_token_offsets).to(DEV)
+    dco = torch.from_numpy(dco_h).to(DEV)
+    Kb, Vb, Rb = msa.encode_pool(mem.K, mem.V, mem.KR, dto, dco, C, d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(104)
+    offs = mem.doc_token_offsets
+    docs = _sample_docs(rng, N, chains[0], 10)
+    for i in docs:
+        t0, t1 = int(offs[i]), int(offs[i + 1])
+        oK, oV, oR, _ = O.pool(u16(mem.K[t0:t1]), u16(mem.V[t0:t1]), u16(mem.KR[t0:t1]),
+                               np.array([0, t1 - t0]))
+        r0, r1 = int(dco_h[i]), int(dco_h[i + 1])
+        for g, e, n in ((Kb, oK, "K"), (Vb, oV, "V"), (Rb, oR, "KR")):
+            assert_pooled_close(u16(g[r0:r1]), e, f"doc {i} {n}")
+    max_sel = 16 * int(np.diff(dco_h).max())
+    for qi in (0, len(chains) - 1):
+        il = msa.Interleave(N, cap_loc=3 * 256, d=d)
+        qr_all = []
+        for r, doc in enumerate(chains[qi]):
+            QR, Q, Kn, Vn = synth.cfg5_round(mem, doc, qi, r, device=DEV)
+            out = il.step(Q, Kn, Vn, QR, Rb, Kb, Vb, dco, max_sel)
+            torch.cuda.synchronize()
+            qr_all.append(u16(QR))
+            sel = set(il.topk_ids.cpu().tolist())
+            assert all(c in sel for c in chains[qi][:r + 1]), f"query {qi} round {r}: chain missed"
+            assert torch.isfinite(out.float()).all()
+            # running scores of sampled documents equal routing every token so far
+            sample = _sample_docs(rng, N, chains[qi], 8)
+            exp = _doc_scores_oracle(np.concatenate(qr_all), Rb, dco_h, sample)
+            assert_scores_close(il.doc_scores.cpu().numpy()[sample], exp,
+                                f"query {qi} round {r} running scores")

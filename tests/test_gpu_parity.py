@@ -116,7 +116,8 @@ def _check_route(QR, st, d, accumulate=False, prev=None):
     return ds, ids, worst
 
 
-@pytest.mark.parametrize("B,M", [(1, 1), (3, 1), (2, 3), (1, 8), (5, 13), (1, 64), (9, 1)])
+@pytest.mark.parametrize("B,M", [(1, 1), (3, 1), (2, 3), (1, 8), (5, 13), (1, 64), (9, 1),
+                                 (64, 1), (1, 130), (3, 70), (70, 1)])
 def test_route_shapes(B, M):
     _banner(f"route B={B} M={M}")
     st = _store(3000, 21 + B * 100 + M)
@@ -138,10 +139,11 @@ def test_route_cfg1_planted():
     assert set(ids.cpu().numpy()[0][:4].tolist()) == set(mem.planted.keys())
 
 
-def test_route_mean_mode():
-    _banner("route MEAN")
+@pytest.mark.parametrize("B,M", [(2, 11), (1, 3), (2, 100)])
+def test_route_mean_mode(B, M):
+    _banner(f"route MEAN B={B} M={M}")
     st = _store(2000, 31)
-    QR = synth.randn_bf16((2, 11, 8, 128), synth.torch_gen(6, 1))
+    QR = synth.randn_bf16((B, M, 8, 128), synth.torch_gen(6, M))
     _check_route(QR, st, msa.dims(token_reduce=O.TOKEN_REDUCE_MEAN))
 
 
