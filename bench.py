@@ -26,6 +26,8 @@ Other workloads (--workload) measure single stages for the design notes:
   pool10m     Stage-1 pooling of 10M raw tokens (K, V, K^R, 61.4 GB read)
   interleave  3 Memory-Interleave rounds (256 new tokens each) for 32 queries
               over a pooled 10M-token memory
+  copy        a plain 2 GiB device-to-device copy: the known-size reference
+              that scales the FETCH_SIZE / WRITE_SIZE counters into HBM bytes
 """
 from __future__ import annotations
 
@@ -50,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", choices=["100m", "route16m", "pool10m", "interleave"],
+    ap.add_argument("--workload", choices=["100m", "route16m", "pool10m", "interleave", "copy"],
                     default="100m")
     ap.add_argument("--layers", type=int, default=18)
     ap.add_argument("--chunks", type=int, default=1_562_500)
@@ -66,19 +68,22 @@ def log(args, msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def stored_traffic(name, kernel_src):
+def stored_traffic(name, kernel_srcs):
     """HBM bytes per launch measured with rocprofv3 counters (profiles/), used
-    only while the kernel source is unchanged since the measurement."""
+    only while the kernel's sources are unchanged since the measurement."""
     p = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(p):
         return None
     t = json.load(open(p))
-    if t.get("source_sha256") != source_sha(kernel_src):
+    if t.get("source_sha256") != source_sha(kernel_srcs):
         return None
     return t.get("bytes_per_launch")
 
@@ -270,7 +275,8 @@ def workload_100m(args):
         "roofline": {"bound": "hbm", "kernel": "scan_valu_kernel<1> (msa_route_scores)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": stored_traffic("route_scan", csrc("msa_route.hip")),
+                     "traffic": stored_traffic("route_scan", [csrc("msa_route.hip"),
+                                                                csrc("msa_internal.h")]),
                      "bytes_per_launch": scan_bytes},
     })
     if not args.no_cpu_baseline:
@@ -332,7 +338,8 @@ def workload_route16m(args):
         "roofline": {"bound": "hbm", "kernel": "scan_mfma_kernel (msa_route_scores)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": stored_traffic("route_mfma", csrc("msa_route_mfma.hip")),
+                     "traffic": stored_traffic("route_mfma", [csrc("msa_route_mfma.hip"),
+                                                                csrc("msa_internal.h")]),
                      "bytes_per_launch": C * ROW_BYTES,
                      "algorithmic_tflops": 2.0 * B * C * 1024 / (scan_us * 1e-6) / 1e12},
     })
@@ -398,7 +405,7 @@ def workload_pool10m(args):
         "roofline": {"bound": "hbm", "kernel": "pool_kernel (msa_encode_pool)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": stored_traffic("pool", csrc("msa_pool.hip")),
+                     "traffic": stored_traffic("pool", [csrc("msa_pool.hip"), csrc("msa_internal.h")]),
                      "bytes_per_launch": nbytes},
     })
     if not args.no_cpu_baseline:
@@ -485,6 +492,37 @@ def workload_interleave(args):
     return r
 
 
+# ---------------------------------------------------------------------------
+# copy: a known-size copy that calibrates the HBM byte counters
+# ---------------------------------------------------------------------------
+def workload_copy(args):
+    import torch
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(7)
+    dst = torch.empty_like(src)
+
+    def step(tm):
+        e0 = tm.ev() if tm else None
+        dst.copy_(src)
+        if tm:
+            tm.add("copy", e0, tm.ev())
+
+    tm = Timer()
+    ms = run_timed(args, step, tm)
+    us = tm.avg_us("copy")
+    r = base_result(args, "bytes copied/sec", n / (ms * 1e-3), "B/s", ms,
+                    {"workload": "2 GiB device-to-device copy (counter calibration)",
+                     "bytes": n})
+    r.update({"copy_us": us, "roofline": {"bound": "hbm", "kernel": "device copy",
+                                          "achieved": 2 * n / (us * 1e-6) / 1e9,
+                                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                          "frac": 2 * n / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                          "traffic": None, "bytes_per_launch": 2 * n},
+              "cpu_baseline": None})
+    return r
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -496,7 +534,7 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     fn = {"100m": workload_100m, "route16m": workload_route16m, "pool10m": workload_pool10m,
-          "interleave": workload_interleave}[args.workload]
+          "interleave": workload_interleave, "copy": workload_copy}[args.workload]
     print(json.dumps(fn(args)), flush=True)
 
 
