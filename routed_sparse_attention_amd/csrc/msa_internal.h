@@ -49,10 +49,10 @@ __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uin
 
 // float -> bf16, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  // NaN stays NaN (quiet bit set); selects, not branches, so callers unroll
+  return (uint16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : rne);
 }
 
 // double -> bf16 with a single rounding (nearest even): first narrow to float
@@ -60,11 +60,11 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 // odd"), then round that float to bf16. Float keeps 24 bits, more than bf16's
 // 8 + 2, so the two steps round exactly once.
 __device__ __forceinline__ uint16_t d2bf(double x) {
-  if (x != x) return 0x7fc0u;
-  float f = __double2float_rz(x);
+  const float f = __double2float_rz(x);
   uint32_t u = __float_as_uint(f);
-  if ((double)f != x && (u & 0x7fffffffu) < 0x7f800000u) u |= 1u;
-  return f2bf(__uint_as_float(u));
+  u |= ((double)f != x && (u & 0x7fffffffu) < 0x7f800000u) ? 1u : 0u;
+  const uint16_t b = f2bf(__uint_as_float(u));
+  return (x != x) ? (uint16_t)0x7fc0u : b;
 }
 
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
@@ -165,6 +165,8 @@ struct PoolArgs {
   int32_t n_docs; int64_t n_tokens; int64_t n_chunks; int32_t chunk;
   double theta; int32_t rope_mode;
   uint16_t* Kbar; uint16_t* Vbar; uint16_t* KRbar;
+  // filled by launch_pool (fp64, host): one-step rotations per frequency m
+  double cw[64], sw[64];     // cos ω_m, sin ω_m
 };
 int launch_pool(const PoolArgs& a, hipStream_t s);
 
@@ -207,7 +209,7 @@ __host__ __device__ inline TileRows tile_rows_of(const RouteGeom& g, int ty) {
 // (MEAN already divided by M); with parts > 1 they write per-part partials
 // P[parts][B][C] (max, or sums under MEAN) that launch_parts_combine folds.
 constexpr int kValuTileRows = 8;
-constexpr int kMfmaTileRows = 64;
+constexpr int kMfmaTileRows = 16;   // one segment per MFMA lane group
 int launch_scan_valu(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRbar,
                      int64_t n_chunks, int32_t token_reduce, float* out, hipStream_t s);
 int launch_scan_mfma(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRbar,

@@ -10,8 +10,9 @@
 // token count; output is rounded to bf16 (the caches are BF16).
 //
 // Design (HBM-bound stream, 6 KiB read per token):
-//   - one workgroup of 3 waves handles kChunksPerWG consecutive chunks; wave 0
-//     pools K, wave 1 V, wave 2 K^R, so no wave diverges;
+//   - each wave pools kChunksPerWave consecutive chunks of one tensor; V and
+//     K^R go through a plain-mean instantiation and K through the RoPE one,
+//     so the plain pass keeps its register count (and occupancy) low;
 //   - lane (h, p) = (lane/8, lane%8) owns dims [8p, 8p+8) and [64+8p, 64+8p+8)
 //     of head h: both halves of every rotation pair it needs arrive in its own
 //     two 16-byte loads, so RoPE needs no cross-lane exchange;
@@ -19,15 +20,21 @@
 //     fp32 add, and fp64 makes the bf16 result the correctly rounded mean
 //     (the fp32 error of a 64-term sum can exceed one bf16 ulp when the mean
 //     is near zero);
-//   - cos/sin of t·ω advance by an fp64 angle-addition step per token; only a
-//     workgroup's first chunk (if it starts mid-document) needs a sincos.
+//   - cos/sin of t·ω advance by an fp64 angle-addition step per token; the
+//     host supplies cos ω_m, sin ω_m in fp64, and a chunk that does not
+//     continue the previous one (a wave's first chunk, CHUNK mode) reaches its
+//     angle by square-and-multiply of that one-step rotation;
+//   - token loads are branch-free (clamped indices, masked values), so a
+//     group of tokens' loads (8 plain, 4 with RoPE) is in flight at once.
+#include <cmath>
+
 #include "msa_internal.h"
 
 namespace msa {
 namespace {
 
-constexpr int kChunksPerWG = 8;
-constexpr int kUnroll = 4;
+constexpr int kChunksPerWave = 4;
+constexpr int kWavesPerWG = 4;
 
 // Largest i in [0, n_docs-1] with dco[i] <= c (document holding chunk c).
 __device__ int find_doc(const int64_t* dco, int n_docs, int64_t c) {
@@ -37,6 +44,24 @@ __device__ int find_doc(const int64_t* dco, int n_docs, int64_t c) {
     if (dco[mid] <= c) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// (cos, sin) of n·ω from (cos ω, sin ω) by square-and-multiply (n >= 0).
+__device__ __forceinline__ void rot_pow(double c1, double s1, int64_t n, double& c, double& s) {
+  c = 1.0;
+  s = 0.0;
+  double bc = c1, bs = s1;
+  while (n > 0) {
+    if (n & 1) {
+      const double t = c * bc - s * bs;
+      s = s * bc + c * bs;
+      c = t;
+    }
+    const double t = bc * bc - bs * bs;
+    bs = 2.0 * bc * bs;
+    bc = t;
+    n >>= 1;
+  }
 }
 
 __device__ __forceinline__ void unpack8(const uint4& x, double* v) {
@@ -55,28 +80,35 @@ __device__ __forceinline__ uint4 pack8(const double* m) {
   return r;
 }
 
-__global__ __launch_bounds__(192) void pool_kernel(PoolArgs a) {
-  const int wave = threadIdx.x >> 6;  // 0: K, 1: V, 2: K^R
+// One wave pools kChunksPerWave consecutive chunks of one tensor. ROPE: the
+// tensor is K and carries document RoPE (TOKEN or CHUNK mode); otherwise a
+// plain mean (V, K^R). Lane (h, p) = (lane/8, lane%8) owns dims [8p, 8p+8)
+// and [64+8p, 64+8p+8) of head h.
+template <bool ROPE, int kUnroll>
+__global__ __launch_bounds__(256) void pool_kernel(PoolArgs a, int32_t first_tensor) {
+  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int h = lane >> 3, p = lane & 7;
   const int idx0 = h * 16 + p;        // 16-byte vector holding dims 8p..8p+7
   const int idx1 = idx0 + 8;          // dims 64+8p..64+8p+7
-  const uint16_t* src = wave == 0 ? a.K : (wave == 1 ? a.V : a.KR);
-  uint16_t* dst = wave == 0 ? a.Kbar : (wave == 1 ? a.Vbar : a.KRbar);
+  const int tensor = first_tensor + (int)blockIdx.y;   // 0: K, 1: V, 2: K^R
+  const uint16_t* src = tensor == 0 ? a.K : (tensor == 1 ? a.V : a.KR);
+  uint16_t* dst = tensor == 0 ? a.Kbar : (tensor == 1 ? a.Vbar : a.KRbar);
   if (dst == nullptr) return;
-  const int64_t c_begin = (int64_t)blockIdx.x * kChunksPerWG;
+  const int64_t c_begin = ((int64_t)blockIdx.x * kWavesPerWG + wave) * kChunksPerWave;
   if (c_begin >= a.n_chunks) return;
-  const int64_t c_end = min(c_begin + (int64_t)kChunksPerWG, a.n_chunks);
-  const bool tok_rope = (wave == 0) && a.rope_mode == MSA_DOC_ROPE_TOKEN;
-  const bool chunk_rope = (wave == 0) && a.rope_mode == MSA_DOC_ROPE_CHUNK;
+  const int64_t c_end = min(c_begin + (int64_t)kChunksPerWave, a.n_chunks);
+  const bool tok_rope = ROPE && a.rope_mode == MSA_DOC_ROPE_TOKEN;
+  const bool chunk_rope = ROPE && a.rope_mode == MSA_DOC_ROPE_CHUNK;
 
-  // ω_m for this lane's 8 pairs, and the one-step rotation (cos ω, sin ω).
-  double om[8], cw[8], sw[8], cs[8], sn[8];
-  if (wave == 0) {
+  // the one-step rotation (cos ω, sin ω) of this lane's 8 pairs, and the
+  // running rotation (cs, sn) of the current token
+  double cw[8], sw[8], cs[8], sn[8];
+  if (ROPE) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      om[e] = pow(a.theta, -2.0 * (double)(8 * p + e) / (double)kDim);
-      sincos(om[e], &sw[e], &cw[e]);
+      cw[e] = a.cw[8 * p + e];
+      sw[e] = a.sw[8 * p + e];
       cs[e] = 1.0; sn[e] = 0.0;
     }
   }
@@ -98,59 +130,66 @@ __global__ __launch_bounds__(192) void pool_kernel(PoolArgs a) {
     const int64_t pos = j * a.chunk;
 
     if (tok_rope && pos != next_pos) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (pos == 0) { cs[e] = 1.0; sn[e] = 0.0; }
-        else sincos((double)pos * om[e], &sn[e], &cs[e]);
-      }
+      for (int e = 0; e < 8; ++e) rot_pow(cw[e], sw[e], pos, cs[e], sn[e]);
     }
 
     double acc[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.0;
 
+    // Branch-free loads: token indices past the chunk's end are clamped to
+    // its last token (always in bounds) and their values masked out, so all
+    // kUnroll pairs of loads of a group are in flight together.
     const uint4* row = src4 + t0 * kRowVec;
+    const int last = n > 0 ? n - 1 : 0;
     for (int t = 0; t < n; t += kUnroll) {
       uint4 x0[kUnroll], x1[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        if (t + u < n) {
-          x0[u] = load_stream(row + (int64_t)(t + u) * kRowVec + idx0);
-          x1[u] = load_stream(row + (int64_t)(t + u) * kRowVec + idx1);
-        }
+        const int64_t tt = min(t + u, last);
+        x0[u] = load_stream(row + tt * kRowVec + idx0);
+        x1[u] = load_stream(row + tt * kRowVec + idx1);
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        if (t + u < n) {
-          double lo[8], hi[8];
-          unpack8(x0[u], lo);
-          unpack8(x1[u], hi);
-          if (tok_rope) {
+        // a clamped duplicate contributes +0 (its words are zeroed)
+        const uint32_t m = (t + u < n) ? 0xffffffffu : 0u;
+        const uint4 y0 = make_uint4(x0[u].x & m, x0[u].y & m, x0[u].z & m, x0[u].w & m);
+        const uint4 y1 = make_uint4(x1[u].x & m, x1[u].y & m, x1[u].z & m, x1[u].w & m);
+        double lo[8], hi[8];
+        unpack8(y0, lo);
+        unpack8(y1, hi);
+        if (tok_rope) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              acc[e] = fma(lo[e], cs[e], fma(-hi[e], sn[e], acc[e]));
-              acc[8 + e] = fma(hi[e], cs[e], fma(lo[e], sn[e], acc[8 + e]));
-              const double c2 = cs[e] * cw[e] - sn[e] * sw[e];
-              sn[e] = sn[e] * cw[e] + cs[e] * sw[e];
-              cs[e] = c2;
-            }
-          } else {
+          for (int e = 0; e < 8; ++e) {
+            acc[e] = fma(lo[e], cs[e], fma(-hi[e], sn[e], acc[e]));
+            acc[8 + e] = fma(hi[e], cs[e], fma(lo[e], sn[e], acc[8 + e]));
+            const double c2 = cs[e] * cw[e] - sn[e] * sw[e];
+            sn[e] = sn[e] * cw[e] + cs[e] * sw[e];
+            cs[e] = c2;
+          }
+        } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { acc[e] += lo[e]; acc[8 + e] += hi[e]; }
+          for (int e = 0; e < 8; ++e) {
+            acc[e] += lo[e];
+            acc[8 + e] += hi[e];
           }
         }
       }
     }
-    next_pos = pos + n;
+    if (tok_rope) {
+      // the recurrence advanced past the chunk's end by the masked tail steps;
+      // it stays valid only when the chunk was full (the next chunk continues)
+      next_pos = (n % kUnroll == 0) ? pos + n : -1;
+    }
 
     double mean[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) mean[e] = n > 0 ? acc[e] / (double)n : 0.0;
     if (chunk_rope) {
-#pragma unroll
       for (int e = 0; e < 8; ++e) {
-        double s_, c_;
-        sincos((double)j * om[e], &s_, &c_);
+        double c_, s_;
+        rot_pow(cw[e], sw[e], j, c_, s_);
         const double x = mean[e], y = mean[8 + e];
         mean[e] = x * c_ - y * s_;
         mean[8 + e] = y * c_ + x * s_;
@@ -163,11 +202,26 @@ __global__ __launch_bounds__(192) void pool_kernel(PoolArgs a) {
 
 }  // namespace
 
-int launch_pool(const PoolArgs& a, hipStream_t s) {
-  if (a.n_chunks == 0) return MSA_OK;
-  const int64_t n_wg = (a.n_chunks + kChunksPerWG - 1) / kChunksPerWG;
-  hipLaunchKernelGGL(pool_kernel, dim3((unsigned)n_wg), dim3(192), 0, s, a);
-  MSA_LAUNCH_CHECK("pool_kernel launch");
+int launch_pool(const PoolArgs& args, hipStream_t s) {
+  if (args.n_chunks == 0) return MSA_OK;
+  PoolArgs a = args;
+  for (int m = 0; m < 64; ++m) {
+    const double om = std::pow(a.theta, -2.0 * (double)m / (double)kDim);
+    a.cw[m] = std::cos(om);
+    a.sw[m] = std::sin(om);
+  }
+  const int64_t per_wg = (int64_t)kChunksPerWave * kWavesPerWG;
+  const unsigned n_wg = (unsigned)((a.n_chunks + per_wg - 1) / per_wg);
+  // V and K^R (plain means), then K (document RoPE): separate instantiations
+  // so the plain pass does not carry the rotation state's registers
+  if (a.Vbar || a.KRbar) {
+    hipLaunchKernelGGL((pool_kernel<false, 8>), dim3(n_wg, 2), dim3(256), 0, s, a, 1);
+    MSA_LAUNCH_CHECK("pool_kernel<plain> launch");
+  }
+  if (a.Kbar) {
+    hipLaunchKernelGGL((pool_kernel<true, 2>), dim3(n_wg, 1), dim3(256), 0, s, a, 0);
+    MSA_LAUNCH_CHECK("pool_kernel<rope> launch");
+  }
   return MSA_OK;
 }
 

@@ -55,51 +55,45 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 constexpr int kScanWaves = 4;
-constexpr int kScanUnroll = 4;
+// chunks per wave per group: deep for the few-row (decode) tiles, where the
+// registers are free, shallower as the q̂ slices of more rows take them
+constexpr int scan_unroll(int rows) { return rows <= 2 ? 8 : rows <= 4 ? 4 : 2; }
 
 template <int R>
 __global__ __launch_bounds__(256) void scan_valu_kernel(const uint16_t* __restrict__ QR,
                                                         RouteGeom g, const uint4* __restrict__ KR,
                                                         int64_t n_chunks, int32_t token_reduce,
                                                         float* __restrict__ out) {
+  constexpr int kScanUnroll = scan_unroll(R);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const TileRows tr = tile_rows_of(g, blockIdx.y);
   const int n_rows = tr.nq * tr.nr;  // <= R
-  // this lane's slice of every tile row's q̂: [k][0] head lane/16, [k][1] head 4 + lane/16
-  uint4 qh[R][2], ql[R][2];
-#pragma unroll
-  for (int k = 0; k < R; ++k) {
-    if (k < n_rows) {
-      const int64_t row = (int64_t)(tr.b0 + k / tr.nr) * g.M + tr.m0 + k % tr.nr;
-      qhat_hilo_pair(QR + row * kRowElems, lane, qh[k], ql[k]);
-    } else {
-      qh[k][0] = qh[k][1] = ql[k][0] = ql[k][1] = make_uint4(0, 0, 0, 0);
-    }
-  }
+  uint4 qh[R][2], ql[R][2];   // q̂ slices, filled once the first loads are in flight
   const bool mean = token_reduce == MSA_TOKEN_REDUCE_MEAN;
   const float fin = (mean && g.parts == 1) ? 1.0f / (float)g.M : 1.0f;
   const float eps2 = kNormEps * kNormEps;
   const int64_t wave_id = (int64_t)blockIdx.x * kScanWaves + wave;
   const int64_t n_waves = (int64_t)gridDim.x * kScanWaves;
 
-  for (int64_t c0 = wave_id * kScanUnroll; c0 < n_chunks; c0 += n_waves * kScanUnroll) {
-    uint4 k0[kScanUnroll], k1[kScanUnroll];
+  const int64_t stride = n_waves * kScanUnroll;
+  // Loads are branch-free (indices clamped into the store; results past the
+  // end are never stored), so the compiler can wait for exactly the group it
+  // is about to score while the next group, in the other buffer, is in flight.
+  auto load = [&](int64_t cb, uint4* a, uint4* b) {
 #pragma unroll
     for (int u = 0; u < kScanUnroll; ++u) {
-      const int64_t c = c0 + u;
-      if (c < n_chunks) {
-        k0[u] = load_stream(KR + c * kRowVec + lane);
-        k1[u] = load_stream(KR + c * kRowVec + 64 + lane);
-      } else {
-        k0[u] = k1[u] = make_uint4(0, 0, 0, 0);
-      }
+      const int64_t c = min(cb + u, n_chunks - 1);
+      a[u] = load_stream(KR + c * kRowVec + lane);
+      b[u] = load_stream(KR + c * kRowVec + 64 + lane);
     }
+  };
+  auto score = [&](int64_t c0, const uint4* A, const uint4* B) {
 #pragma unroll
     for (int u = 0; u < kScanUnroll; ++u) {
       const int64_t c = c0 + u;
-      const uint32_t ka[4] = {k0[u].x, k0[u].y, k0[u].z, k0[u].w};
-      const uint32_t kb[4] = {k1[u].x, k1[u].y, k1[u].z, k1[u].w};
+      const uint32_t ka[4] = {A[u].x, A[u].y, A[u].z, A[u].w};
+      const uint32_t kb[4] = {B[u].x, B[u].y, B[u].z, B[u].w};
       float na = 0.0f, nb = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -143,6 +137,35 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const uint16_t* __restri
         }
       }
     }
+  };
+  uint4 xa[kScanUnroll], xb[kScanUnroll], ya[kScanUnroll], yb[kScanUnroll];
+  int64_t c0 = wave_id * kScanUnroll;
+  if (c0 >= n_chunks) return;
+  // the first group's loads go out before q̂ is prepared, so that work hides
+  // under their latency
+  load(c0, xa, xb);
+  load(c0 + stride, ya, yb);
+  // this lane's slice of every tile row's q̂: [k][0] head lane/16, [k][1] head 4 + lane/16
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if (k < n_rows) {
+      const int64_t row = (int64_t)(tr.b0 + k / tr.nr) * g.M + tr.m0 + k % tr.nr;
+      qhat_hilo_pair(QR + row * kRowElems, lane, qh[k], ql[k]);
+    } else {
+      qh[k][0] = qh[k][1] = ql[k][0] = ql[k][1] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  // x holds group c0, y group c0 + stride; a buffer is refilled as soon as
+  // it has been scored
+  while (true) {
+    score(c0, xa, xb);
+    c0 += stride;
+    if (c0 >= n_chunks) break;
+    load(c0 + stride, xa, xb);
+    score(c0, ya, yb);
+    c0 += stride;
+    if (c0 >= n_chunks) break;
+    load(c0 + stride, ya, yb);
   }
 }
 
@@ -170,14 +193,17 @@ __global__ __launch_bounds__(256) void parts_combine_kernel(const float* __restr
 int launch_scan_valu(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRbar,
                      int64_t n_chunks, int32_t token_reduce, float* out, hipStream_t s) {
   if (n_chunks == 0 || g.n_tiles == 0) return MSA_OK;
-  // at most 2048 workgroups (8 per CU); each wave strides over the store
-  const int64_t per_wg = (int64_t)kScanWaves * kScanUnroll;
-  int64_t wg = (n_chunks + per_wg - 1) / per_wg;
-  if (wg > 2048) wg = 2048;
-  const dim3 grid((unsigned)wg, (unsigned)g.n_tiles);
   const uint4* kr = reinterpret_cast<const uint4*>(KRbar);
   // rows actually present in a tile (a lone decode query must not pay for 8)
   const int rows = g.parts == 1 ? (g.q_per_tile < g.B ? g.q_per_tile : g.B) * g.M : g.tile_rows;
+  // At most 8192 workgroups (32 per CU, run in turn); each wave strides over
+  // the store. Fewer leave the HBM queues short near the end of the scan, more
+  // repeat the per-wave q̂ preparation too often (measured on the 1.56M-chunk
+  // decode scan: 2048 → 500 µs, 8192 → 470 µs, 16384 → 520 µs).
+  const int64_t per_wg = (int64_t)kScanWaves * scan_unroll(rows);
+  int64_t wg = (n_chunks + per_wg - 1) / per_wg;
+  if (wg > 8192) wg = 8192;
+  const dim3 grid((unsigned)wg, (unsigned)g.n_tiles);
   if (rows <= 1)
     hipLaunchKernelGGL(scan_valu_kernel<1>, grid, dim3(256), 0, s, QR, g, kr, n_chunks, token_reduce, out);
   else if (rows <= 2)
