@@ -7,10 +7,12 @@
 // all are selected; a NaN score ranks below every number.
 //
 // Design.
-//   doc_max: one thread per (document, query); each thread reads its chunk
-//     range with 16 independent loads in flight and max-reduces it (NaN
-//     propagates, as numpy's max does), max-merges with the previous score
-//     when accumulating, and writes the document score.
+//   doc_max: a workgroup per (256 documents, query). The documents' chunk
+//     range is contiguous; it streams through a 32 KiB LDS tile with
+//     coalesced loads (all 32 loads of a thread in flight), then each thread
+//     max-reduces its own document's chunks from LDS (NaN propagates, as
+//     numpy's max does), max-merges with the previous score when
+//     accumulating, and writes the document score.
 //   topk_select: one 1024-thread workgroup per query. Each document becomes
 //     the unique 64-bit key (order-preserving uint32 of the score) << 32 |
 //     (0xFFFFFFFF − id), so larger key = better document and equal scores
@@ -19,7 +21,10 @@
 //     documents. T = the k-th best block maximum is reached by at least k
 //     documents, and only blocks whose maximum reaches T (about k of them)
 //     can hold a key >= T; those keys are ballot-compacted into LDS and
-//     bitonic-sorted, and the head of the list is the answer.
+//     sorted, and the head of the list is the answer. Keys are distinct (the
+//     id is part of the key), so lists of up to 256 keys are sorted in one
+//     step by rank counting (each key's rank = number of larger keys);
+//     longer ones by a bitonic network.
 //     Fallback (massive ties at T, or more than 2048 blocks):
 //     radix select on the uint32 score keys. Four passes
 //     over 8-bit digits, most significant first, histogram the keys that
@@ -53,29 +58,51 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// The 256 documents of a block own one contiguous chunk range (the chunk
+// plan keeps documents contiguous). The block streams that range through an
+// LDS tile with coalesced loads; each thread then takes the max over its own
+// document's chunks in the tile.
+constexpr int kDocTile = 8192;   // chunk scores per LDS tile (32 KiB)
+constexpr int kDocLoads = kDocTile / kMaxThreads;   // 32 loads per thread, all in flight
+
 __global__ __launch_bounds__(256) void doc_max_kernel(const float* __restrict__ S, int64_t C,
                                                       const int64_t* __restrict__ dco,
                                                       int32_t n_docs,
                                                       float* __restrict__ doc_scores,
                                                       int32_t accumulate,
                                                       uint64_t* __restrict__ bmax) {
+  __shared__ float tile[kDocTile];
   __shared__ uint64_t wbest[kMaxThreads / 64];
   const int b = blockIdx.y;
-  const int64_t i = (int64_t)blockIdx.x * kMaxThreads + threadIdx.x;
+  const int64_t d0 = (int64_t)blockIdx.x * kMaxThreads;
+  const int64_t d1 = min(d0 + kMaxThreads, (int64_t)n_docs);
+  const int64_t i = d0 + threadIdx.x;
+  auto clampc = [&](int64_t c) { return max((int64_t)0, min(c, C)); };
+  const int64_t r0 = clampc(dco[d0]), r1 = max(r0, clampc(dco[d1]));
+  int64_t c0 = 0, c1 = 0;
+  if (i < n_docs) {
+    c0 = clampc(dco[i]);
+    c1 = max(c0, clampc(dco[i + 1]));
+  }
+  const float* Sb = S + (int64_t)b * C;
+  float s = -INFINITY;
+  for (int64_t t0 = r0; t0 < r1; t0 += kDocTile) {
+    const int n = (int)min((int64_t)kDocTile, r1 - t0);
+    // every load is issued before any store waits on one (indices past the
+    // range are clamped into it and never read back)
+    float v[kDocLoads];
+#pragma unroll
+    for (int u = 0; u < kDocLoads; ++u) v[u] = Sb[t0 + min((int)threadIdx.x + u * kMaxThreads, n - 1)];
+#pragma unroll
+    for (int u = 0; u < kDocLoads; ++u) tile[threadIdx.x + u * kMaxThreads] = v[u];
+    __syncthreads();
+    const int a = (int)(max(c0, t0) - t0), e = (int)(min(c1, t0 + n) - t0);
+#pragma unroll 8
+    for (int c = a; c < e; ++c) s = nan_max(s, tile[c]);
+    __syncthreads();
+  }
   uint64_t key = 0;
   if (i < n_docs) {
-    int64_t c0 = dco[i], c1 = dco[i + 1];
-    c0 = max((int64_t)0, min(c0, C));
-    c1 = max(c0, min(c1, C));
-    const float* Sb = S + (int64_t)b * C;
-    float s = -INFINITY;
-    for (int64_t c = c0; c < c1; c += 16) {
-      float v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = (c + u < c1) ? Sb[c + u] : -INFINITY;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) s = nan_max(s, v[u]);
-    }
     float* ds = doc_scores + (int64_t)b * n_docs + i;
     if (accumulate) s = nan_max(*ds, s);
     *ds = s;
@@ -197,6 +224,36 @@ __device__ void bitonic_desc(uint64_t* a, int n2) {
   }
 }
 
+// Sorts n <= kSelThreads distinct keys of a[] descending into out[] (a and
+// out must not overlap): a key's rank is the number of larger keys.
+constexpr int kRankMax = 256;
+__device__ void rank_sort_desc(const uint64_t* a, uint64_t* out, int n) {
+  const int tid = threadIdx.x;
+  if (tid < n) {
+    const uint64_t x = a[tid];
+    int r = 0;
+    for (int j = 0; j < n; ++j) r += a[j] > x ? 1 : 0;
+    out[r] = x;
+  }
+  __syncthreads();
+}
+
+// Sorts cand[0..n) descending in place (cand has room for kCandCap keys;
+// rank sorting uses the upper half as its output).
+__device__ void sort_cand_desc(uint64_t* cand, int n) {
+  if (n <= kRankMax) {
+    rank_sort_desc(cand, cand + kCandCap / 2, n);
+    if (threadIdx.x < n) cand[threadIdx.x] = cand[kCandCap / 2 + threadIdx.x];
+    __syncthreads();
+    return;
+  }
+  int n2 = 1;
+  while (n2 < n) n2 <<= 1;
+  for (int i = n + threadIdx.x; i < n2; i += kSelThreads) cand[i] = 0;
+  __syncthreads();
+  bitonic_desc(cand, n2);
+}
+
 __global__ __launch_bounds__(1024) void topk_select_kernel(const float* __restrict__ doc_scores,
                                                            const uint64_t* __restrict__ bmax,
                                                            int32_t n_blocks, int32_t N,
@@ -222,57 +279,50 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(const float* __restri
   if (n_blocks >= K && n_blocks <= kCandCap) {
     // ---- T = K-th best block maximum: at least K documents reach it, and a
     //      document at or above T can only sit in a block whose maximum does
-    int n2 = 1;
-    while (n2 < n_blocks) n2 <<= 1;
-    for (int i = tid; i < n2; i += kSelThreads) cand[i] = i < n_blocks ? bm[i] : 0ull;
+    for (int i = tid; i < n_blocks; i += kSelThreads) cand[i] = bm[i];
     if (tid == 0) n_cand = 0;
     __syncthreads();
-    bitonic_desc(cand, n2);
+    sort_cand_desc(cand, n_blocks);
     const uint64_t T = cand[K - 1];
-    int n_hot = 0;  // blocks whose maximum reaches T (a prefix of the sorted list)
-    for (int i = 0; i < n_blocks && cand[i] >= T; ++i) ++n_hot;
-    // block ids of the hot blocks, from their maximum's document id
-    int hot_blk = -1;
-    if (tid < n_hot) hot_blk = (int)((0xFFFFFFFFu - (uint32_t)(cand[tid] & 0xFFFFFFFFu)) / kMaxThreads);
-    // ---- gather keys >= T from the hot blocks (256 documents each)
-    if (n_hot <= kMaxHot) {
-      if (tid < n_hot) hot[tid] = hot_blk;
-      __syncthreads();
-      const int total = n_hot * kMaxThreads;
-      for (int base = 0; base < total; base += kSelThreads) {
-        const int j = base + tid;
-        uint64_t k = 0;
-        bool c = false;
-        if (j < total) {
-          const int64_t i = (int64_t)hot[j / kMaxThreads] * kMaxThreads + (j % kMaxThreads);
-          if (i < N) {
-            k = doc_key(s[i], i);
-            c = k >= T;
-          }
-        }
-        const uint64_t m = __ballot(c);
-        if (m) {
-          int pos0 = 0;
-          if (lane == 0) pos0 = atomicAdd(&n_cand, (int)__popcll(m));
-          pos0 = __shfl(pos0, 0);
-          const int pos = pos0 + (int)__popcll(m & ((1ull << lane) - 1ull));
-          if (c && pos < kCandCap) cand[pos] = k;
-        }
+    // block maxima are distinct, so exactly the first K blocks reach T
+    const int n_hot = K;
+    if (tid < n_hot) hot[tid] = (int)((0xFFFFFFFFu - (uint32_t)(cand[tid] & 0xFFFFFFFFu)) / kMaxThreads);
+    __syncthreads();
+    // ---- gather keys >= T from the hot blocks (256 documents each); every
+    //      load of a thread is issued before the compaction
+    constexpr int kPer = kMaxK * kMaxThreads / kSelThreads;
+    const int total = n_hot * kMaxThreads;
+    uint64_t kk[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = u * kSelThreads + tid;
+      kk[u] = 0;
+      if (j < total) {
+        const int64_t i = (int64_t)hot[j / kMaxThreads] * kMaxThreads + (j % kMaxThreads);
+        if (i < N) kk[u] = doc_key(s[i], i);
       }
-      __syncthreads();
-      cnt = n_cand;
     }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const bool c = kk[u] >= T && kk[u] != 0;   // kk = 0 past `total`
+      const uint64_t m = __ballot(c);
+      if (m) {
+        int pos0 = 0;
+        if (lane == 0) pos0 = atomicAdd(&n_cand, (int)__popcll(m));
+        pos0 = __shfl(pos0, 0);
+        const int pos = pos0 + (int)__popcll(m & ((1ull << lane) - 1ull));
+        if (c && pos < kCandCap / 2) cand[pos] = kk[u];
+      }
+    }
+    __syncthreads();
+    cnt = n_cand <= kCandCap / 2 ? n_cand : kCandCap + 1;
   } else if (N <= kCandCap) {
     for (int i = tid; i < N; i += kSelThreads) cand[i] = doc_key(s[i], i);
     cnt = N;
     __syncthreads();
   }
   if (cnt <= kCandCap) {
-    int n2 = 1;
-    while (n2 < cnt) n2 <<= 1;
-    for (int i = cnt + tid; i < n2; i += kSelThreads) cand[i] = 0;
-    __syncthreads();
-    bitonic_desc(cand, n2);
+    sort_cand_desc(cand, cnt);
   } else {
     // massive ties at the threshold (or an unusual shape): radix select into
     // cand[kMaxK..), then rank into cand[0..Ks)
