@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", choices=["100m", "route16m", "pool10m", "interleave", "copy"],
+    ap.add_argument("--workload", choices=["100m", "route16m", "pool10m", "interleave", "store",
+                                           "copy"],
                     default="100m")
     ap.add_argument("--layers", type=int, default=18)
     ap.add_argument("--chunks", type=int, default=1_562_500)
@@ -200,7 +201,7 @@ def cpu_baseline_100m(args, store, n_layers, query, att0):
     t_layer = t_route * (C / sample) + t_select + t_attend
     return {
         "value": C * TOKENS_PER_CHUNK / t_layer, "unit": "tokens/s", "cores": 1, "host_cores_available": host_cores(), "blas_threads": 1,
-        "kind": "oracle",
+                             "kind": "oracle",
         "sample": (f"oracle routing over {sample:,} of {C:,} chunks of layer 0 "
                    f"({t_route:.2f} s, scaled to the full layer), document max + top-16 over "
                    f"{store.n_docs:,} documents ({t_select:.2f} s) and sparse attention for one "
@@ -454,7 +455,7 @@ def workload_pool10m(args):
             O.pool(K, V, R, offs[:docs[-1] + 2], docs=docs)
             t = time.perf_counter() - t0
         r["cpu_baseline"] = {"value": tok / t, "unit": "tokens/s", "cores": 1, "host_cores_available": host_cores(), "blas_threads": 1,
-        "kind": "oracle",
+                             "kind": "oracle",
                              "sample": f"oracle pooling of the first {len(docs)} documents "
                                        f"({tok:,} tokens, {t:.2f} s); numpy fp64, 1 thread"}
     else:
@@ -554,6 +555,85 @@ def workload_copy(args):
     return r
 
 
+# ---------------------------------------------------------------------------
+# store: streaming memory update — the 10M-token memory appended in batches
+# ---------------------------------------------------------------------------
+def workload_store(args):
+    import tempfile
+
+    import numpy as np
+    import torch
+
+    import routed_sparse_attention_amd as msa
+    import synth
+
+    dev = "cuda"
+    mem, _ = synth.cfg5_memory(dev)
+    d = msa.dims()
+    offs = mem.doc_token_offsets
+    N, T = mem.n_docs, mem.n_tokens
+    dco_h = msa.plan_chunks(offs)
+    C = int(dco_h[-1])
+    n_batches = 10
+    cuts = [int(x) for x in np.linspace(0, N, n_batches + 1)]
+    batches = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        t0, t1 = int(offs[a]), int(offs[b])
+        batches.append((mem.K[t0:t1], mem.V[t0:t1], mem.KR[t0:t1], offs[a:b + 1] - offs[a]))
+    st = msa.Store(N, C, d=d)
+
+    def step(tm):
+        st.reset()
+        e0 = tm.ev() if tm else None
+        for K, V, KR, o in batches:
+            st.append(K, V, KR, o)
+        if tm:
+            tm.add("grow", e0, tm.ev())
+
+    tm = Timer()
+    ms = run_timed(args, step, tm)
+    torch.cuda.synchronize()
+    # the grown store is the one-shot encode, bit for bit
+    dto = torch.from_numpy(offs).to(dev)
+    dco = torch.from_numpy(dco_h).to(dev)
+    ref = msa.encode_pool(mem.K, mem.V, mem.KR, dto, dco, C, d)
+    same = all(torch.equal(a.view(torch.int16), b.view(torch.int16))
+               for a, b in zip((st.Kbar, st.Vbar, st.KRbar), ref))
+    assert same and np.array_equal(st.offsets_h, dco_h), "grown store differs from one encode"
+    del ref
+    grow_us = tm.avg_us("grow")
+    nbytes = 3 * ROW_BYTES * (T + C)
+    achieved = nbytes / (grow_us * 1e-6) / 1e9
+    # save and load through a file (one pass each, wall clock, synchronous calls)
+    file_bytes = 3 * ROW_BYTES * C + 8 * (N + 1) + 64
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "memory.msastore")
+        t0 = time.perf_counter()
+        st.save(path)
+        t_save = time.perf_counter() - t0
+        back = msa.Store(N, C, d=d)
+        t0 = time.perf_counter()
+        back.load(path)
+        t_load = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        assert torch.equal(back.KRbar.view(torch.int16), st.KRbar.view(torch.int16))
+        del back
+    r = base_result(args, "memory tokens appended/sec", T / (ms * 1e-3), "tokens/s", ms,
+                    {"workload": f"streaming update: {T / 1e6:.0f}M raw tokens ({N:,} documents) "
+                                 f"appended to an empty store in {n_batches} batches",
+                     "tokens": T, "chunks": C, "documents": N, "batches": n_batches})
+    r.update({
+        "grow_us": grow_us, "equals_one_shot_encode": True,
+        "save_s": t_save, "load_s": t_load, "file_bytes": file_bytes,
+        "save_gb_s": file_bytes / t_save / 1e9, "load_gb_s": file_bytes / t_load / 1e9,
+        "roofline": {"bound": "hbm", "kernel": "pool_kernel (msa_store_append, 10 calls)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": nbytes},
+        "cpu_baseline": None,
+    })
+    return r
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -565,6 +645,7 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     fn = {"100m": workload_100m, "route16m": workload_route16m, "pool10m": workload_pool10m,
+          "store": workload_store,
           "interleave": workload_interleave, "copy": workload_copy}[args.workload]
     print(json.dumps(fn(args)), flush=True)
 

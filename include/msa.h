@@ -61,7 +61,8 @@ typedef enum msa_status {
   MSA_ERR_SHAPE = -2,       /* sizes inconsistent or out of range */
   MSA_ERR_WORKSPACE = -3,   /* workspace missing or too small */
   MSA_ERR_HIP = -4,         /* a HIP runtime call or launch failed */
-  MSA_ERR_UNSUPPORTED = -5  /* valid but not implemented (e.g. head_dim != 128) */
+  MSA_ERR_UNSUPPORTED = -5, /* valid but not implemented (e.g. head_dim != 128) */
+  MSA_ERR_IO = -6           /* a store file could not be read or written, or is malformed */
 } msa_status;
 
 enum { MSA_TOKEN_REDUCE_MAX = 0, MSA_TOKEN_REDUCE_MEAN = 1 };
@@ -98,7 +99,7 @@ const char* msa_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
 int32_t msa_abi_version(void);
-#define MSA_ABI_VERSION 2
+#define MSA_ABI_VERSION 3
 
 /* ------------------------------------------------------------------------ */
 /* Chunk plan (host, pure). Each document is cut into ceil(n_i / chunk)
@@ -248,6 +249,79 @@ int32_t msa_interleave_step(const msa_dims* d, msa_interleave_state* st, const m
                             const int64_t* doc_chunk_offsets, int32_t n_docs,
                             int64_t max_sel_chunks, msa_bf16* out, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Streaming memory update: a pooled store that grows by whole documents
+ * without re-encoding what it holds, and its save/load. The pages name the
+ * offline encoding cost of a knowledge base that keeps changing as a
+ * limitation and incremental encoding as a future direction
+ * (paper.rainbus.top, limitations and future-directions sections); pooling
+ * is per document (techblg section M, routing bullet), so appending the
+ * pooled rows of new documents gives exactly the store of the whole corpus.
+ *
+ * The caller owns every buffer, sized for capacity:
+ *   Kbar, Vbar [cap_chunks, n_kv_heads, 128] bf16: device memory, or pinned
+ *     host memory (the K̄/V̄ host tier); either may be NULL (not kept).
+ *   KRbar [cap_chunks, n_router_heads, 128] bf16, device; may be NULL.
+ *   doc_chunk_offsets [cap_docs+1] int64, device; doc_chunk_offsets_h, its
+ *     host mirror [cap_docs+1] (pinned memory keeps the uploads asynchronous).
+ * n_docs / n_chunks are host fields maintained by the calls below; rows
+ * [0, n_chunks) and offsets [0, n_docs] are valid once the stream that last
+ * wrote them has been synchronised. The store is used by the routing and
+ * attention calls like any pooled memory (KRbar, Kbar, Vbar, n_chunks,
+ * doc_chunk_offsets, n_docs). */
+typedef struct msa_store {
+  msa_bf16* Kbar;
+  msa_bf16* Vbar;
+  msa_bf16* KRbar;
+  int64_t* doc_chunk_offsets;
+  int64_t* doc_chunk_offsets_h;
+  int64_t cap_chunks;
+  int32_t cap_docs;
+  int32_t n_docs;
+  int64_t n_chunks;
+} msa_store;
+
+/* Empties the store: n_docs = n_chunks = 0 and offset 0 (host and device)
+ * set to 0. */
+int32_t msa_store_reset(msa_store* st, void* stream);
+
+/* Appends n_new documents. K, V, KR [n_new_tokens, H, 128] bf16 (device) are
+ * their raw states (an input may be NULL when the store does not keep that
+ * tensor); doc_token_offsets [n_new+1] (device) and doc_token_offsets_h (host)
+ * are their token offsets from 0. The new documents get ids n_docs ..
+ * n_docs+n_new-1 and chunks n_chunks .. ; their rows are pooled exactly as
+ * msa_encode_pool does. MSA_ERR_SHAPE (store unchanged) if the documents or
+ * chunks exceed the capacity; pinned host Kbar/Vbar are written over PCIe. */
+int32_t msa_store_append(const msa_dims* d, msa_store* st, const msa_bf16* K, const msa_bf16* V,
+                         const msa_bf16* KR, const int64_t* doc_token_offsets,
+                         const int64_t* doc_token_offsets_h, int32_t n_new,
+                         int64_t n_new_tokens, void* stream);
+
+/* Store file (little-endian): a 64-byte header — magic "MSASTOR1", u32
+ * version (1), u32 header bytes (64), i32 n_docs, i32 chunk, i64 n_chunks,
+ * i32 heads, i32 head_dim, u32 tensor mask (1 = K̄^R, 2 = K̄, 4 = V̄),
+ * i32 doc_rope_mode, f32 rope_theta, 12 reserved bytes — then the offsets
+ * int64 [n_docs+1], then the present tensors in the order K̄^R, K̄, V̄, each
+ * [n_chunks, heads, head_dim] bf16.
+ *
+ * msa_store_save writes the store's non-NULL tensors; msa_store_load reads a
+ * file into a store whose non-NULL tensors must all be in the file and whose
+ * capacity must hold it (MSA_ERR_SHAPE), with matching chunk size, heads and
+ * head_dim, and, when K̄ is loaded, matching RoPE settings (MSA_ERR_SHAPE).
+ * Both are synchronous (they return when the data is on disk / in the store)
+ * and move the data through the caller's staging buffer (host memory, pinned
+ * for speed, at least 1 MiB). msa_store_file_info reads only the header (no
+ * GPU involved). Any read/write failure or malformed file is MSA_ERR_IO.
+ * Exception to the no-partial-output rule: a load that fails after the
+ * header and offsets were accepted (a truncated tensor section) leaves the
+ * store empty (n_docs = n_chunks = 0). */
+int32_t msa_store_save(const msa_dims* d, const msa_store* st, const char* path,
+                       void* staging_h, size_t staging_bytes);
+int32_t msa_store_load(const msa_dims* d, msa_store* st, const char* path, void* staging_h,
+                       size_t staging_bytes);
+int32_t msa_store_file_info(const char* path, int32_t* n_docs, int64_t* n_chunks,
+                            uint32_t* tensor_mask);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_OK = 0
 STATUS = {0: "MSA_OK", -1: "MSA_ERR_INVALID_ARG", -2: "MSA_ERR_SHAPE", -3: "MSA_ERR_WORKSPACE",
-          -4: "MSA_ERR_HIP", -5: "MSA_ERR_UNSUPPORTED"}
+          -4: "MSA_ERR_HIP", -5: "MSA_ERR_UNSUPPORTED", -6: "MSA_ERR_IO"}
 TOKEN_REDUCE_MAX, TOKEN_REDUCE_MEAN = 0, 1
 DOC_ROPE_TOKEN, DOC_ROPE_CHUNK = 0, 1
 
@@ -28,8 +28,10 @@ EXPORTED = [
     "msa_encode_pool_workspace", "msa_encode_pool", "msa_route_topk_workspace", "msa_route_topk",
     "msa_route_scores_workspace", "msa_route_scores", "msa_select_topk_workspace", "msa_select_topk",
     "msa_sparse_attend_workspace", "msa_sparse_attend", "msa_interleave_reset",
-    "msa_interleave_step_workspace", "msa_interleave_step",
+    "msa_interleave_step_workspace", "msa_interleave_step", "msa_store_reset", "msa_store_append",
+    "msa_store_save", "msa_store_load", "msa_store_file_info",
 ]
+STORE_KR, STORE_K, STORE_V = 1, 2, 4   # tensor bits of a store file
 
 
 class MsaError(RuntimeError):
@@ -52,6 +54,13 @@ class InterleaveStateC(ctypes.Structure):
                 ("n_loc", ctypes.c_int32), ("topk_ids", ctypes.c_void_p),
                 ("topk_scores", ctypes.c_void_p), ("n_sel", ctypes.c_void_p),
                 ("pos0", ctypes.c_int64)]
+
+
+class StoreC(ctypes.Structure):
+    _fields_ = [("Kbar", ctypes.c_void_p), ("Vbar", ctypes.c_void_p), ("KRbar", ctypes.c_void_p),
+                ("doc_chunk_offsets", ctypes.c_void_p), ("doc_chunk_offsets_h", ctypes.c_void_p),
+                ("cap_chunks", ctypes.c_int64), ("cap_docs", ctypes.c_int32),
+                ("n_docs", ctypes.c_int32), ("n_chunks", ctypes.c_int64)]
 
 
 _lib = None
@@ -92,6 +101,13 @@ def lib() -> ctypes.CDLL:
         "msa_interleave_step": (_i32, [_DP, ctypes.POINTER(InterleaveStateC), _vp, _vp, _vp, _vp,
                                        _i32, _vp, _vp, _vp, _i32, _i64, _vp, _i32, _i64, _vp, _vp,
                                        _sz, _vp]),
+        "msa_store_reset": (_i32, [ctypes.POINTER(StoreC), _vp]),
+        "msa_store_append": (_i32, [_DP, ctypes.POINTER(StoreC), _vp, _vp, _vp, _vp, _vp, _i32, _i64,
+                                    _vp]),
+        "msa_store_save": (_i32, [_DP, ctypes.POINTER(StoreC), ctypes.c_char_p, _vp, _sz]),
+        "msa_store_load": (_i32, [_DP, ctypes.POINTER(StoreC), ctypes.c_char_p, _vp, _sz]),
+        "msa_store_file_info": (_i32, [ctypes.c_char_p, ctypes.POINTER(_i32), ctypes.POINTER(_i64),
+                                       ctypes.POINTER(ctypes.c_uint32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -337,3 +353,109 @@ class Interleave:
                                          _p(doc_chunk_offsets), self.n_docs, max_sel_chunks,
                                          _p(out), _p(ws), ws.numel(), _stream()))
         return out
+
+
+# ---------------------------------------------------------------------------
+def store_file_info(path: str) -> tuple[int, int, int]:
+    """(n_docs, n_chunks, tensor bits) from a store file's header."""
+    n_docs, n_chunks, mask = _i32(), _i64(), ctypes.c_uint32()
+    _check(lib().msa_store_file_info(os.fsencode(path), ctypes.byref(n_docs), ctypes.byref(n_chunks),
+                                     ctypes.byref(mask)))
+    return n_docs.value, n_chunks.value, mask.value
+
+
+class Store:
+    """A pooled memory store that grows by whole documents (msa_store_*).
+
+    Buffers are allocated here for the given capacity; ``tensors`` picks which
+    of K̄ ("K"), V̄ ("V") and K̄^R ("KR") are kept; ``kv_on_host`` puts K̄/V̄ in
+    pinned host memory (the host tier). Views of the filled part: ``Kbar``,
+    ``Vbar``, ``KRbar``, ``doc_chunk_offsets`` (device) and ``offsets_h``."""
+
+    def __init__(self, cap_docs: int, cap_chunks: int, d: Dims | None = None,
+                 tensors=("K", "V", "KR"), kv_on_host: bool = False, device="cuda"):
+        self.d = d or dims()
+        self.device = torch.device(device)
+        shape = (cap_chunks, 8, 128)
+
+        def alloc(name, host):
+            if name not in tensors:
+                return None
+            if host:
+                return torch.empty(shape, dtype=torch.bfloat16, pin_memory=True)
+            return torch.empty(shape, dtype=torch.bfloat16, device=self.device)
+
+        self._K = alloc("K", kv_on_host)
+        self._V = alloc("V", kv_on_host)
+        self._KR = alloc("KR", False)
+        self._dco = torch.zeros((cap_docs + 1,), dtype=torch.int64, device=self.device)
+        self._dco_h = torch.zeros((cap_docs + 1,), dtype=torch.int64, pin_memory=True)
+        self.st = StoreC(_p(self._K), _p(self._V), _p(self._KR), _p(self._dco), _p(self._dco_h),
+                         cap_chunks, cap_docs, 0, 0)
+        self.reset()
+
+    def reset(self):
+        _check(lib().msa_store_reset(ctypes.byref(self.st), _stream()))
+
+    @property
+    def n_docs(self) -> int:
+        return self.st.n_docs
+
+    @property
+    def n_chunks(self) -> int:
+        return self.st.n_chunks
+
+    def _view(self, t):
+        return None if t is None else t[: self.n_chunks]
+
+    @property
+    def Kbar(self):
+        return self._view(self._K)
+
+    @property
+    def Vbar(self):
+        return self._view(self._V)
+
+    @property
+    def KRbar(self):
+        return self._view(self._KR)
+
+    @property
+    def doc_chunk_offsets(self) -> torch.Tensor:
+        return self._dco[: self.n_docs + 1]
+
+    @property
+    def offsets_h(self) -> np.ndarray:
+        return self._dco_h[: self.n_docs + 1].numpy().copy()
+
+    def append(self, K, V, KR, doc_token_offsets) -> range:
+        """Pools and appends documents given by their raw states and token
+        offsets (from 0); returns the new documents' ids."""
+        dto_h = np.ascontiguousarray(np.asarray(doc_token_offsets, dtype=np.int64))
+        n_new = len(dto_h) - 1
+        for t, n in ((K, "K"), (V, "V"), (KR, "KR")):
+            if t is not None:
+                _need(t, n, torch.bfloat16, ndim=3)
+        dto = torch.from_numpy(dto_h).to(self.device)
+        first = self.n_docs
+        T = int(dto_h[-1]) if n_new >= 0 else 0
+        _check(lib().msa_store_append(ctypes.byref(self.d), ctypes.byref(self.st),
+                                      _p(K if self._K is not None else None),
+                                      _p(V if self._V is not None else None),
+                                      _p(KR if self._KR is not None else None), _p(dto),
+                                      dto_h.ctypes.data, n_new, T, _stream()))
+        self._keep = (dto, dto_h)   # the uploads read these until the stream catches up
+        return range(first, self.n_docs)
+
+    def _staging(self, nbytes: int):
+        return torch.empty((max(int(nbytes), 1 << 20),), dtype=torch.uint8, pin_memory=True)
+
+    def save(self, path: str, staging_bytes: int = 64 << 20):
+        stg = self._staging(staging_bytes)
+        _check(lib().msa_store_save(ctypes.byref(self.d), ctypes.byref(self.st), os.fsencode(path),
+                                    _p(stg), stg.numel()))
+
+    def load(self, path: str, staging_bytes: int = 64 << 20):
+        stg = self._staging(staging_bytes)
+        _check(lib().msa_store_load(ctypes.byref(self.d), ctypes.byref(self.st), os.fsencode(path),
+                                    _p(stg), stg.numel()))

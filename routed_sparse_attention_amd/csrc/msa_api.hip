@@ -26,8 +26,6 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-namespace {
-
 int check_dims(const msa_dims* d) {
   if (d == nullptr) return fail(MSA_ERR_INVALID_ARG, "dims is NULL");
   if (d->head_dim != kDim)
@@ -77,6 +75,20 @@ int resolve_kv(const void* p, int on_host, const void** out, const char* name) {
   }
   return MSA_OK;
 }
+
+// resolve_kv with the memory kind taken from the pointer itself.
+int resolve_any(const void* p, const void** out, const char* name) {
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MSA_ERR_INVALID_ARG, "%s: not a HIP allocation (%s)", name, hipGetErrorString(e));
+  }
+  return resolve_kv(p, attr.type == hipMemoryTypeHost ? 1 : 0, out, name);
+}
+
+namespace {
 
 // Scan plan: kernel choice (VALU for <= 8 query rows, MFMA above) and the
 // partials buffer needed when a query's tokens span several row tiles.
@@ -245,6 +257,7 @@ int32_t msa_encode_pool(const msa_dims* d, const msa_bf16* K, const msa_bf16* V,
   PoolArgs a;
   a.K = K; a.V = V; a.KR = KR; a.dto = dto; a.dco = dco;
   a.n_docs = n_docs; a.n_tokens = n_tokens; a.n_chunks = n_chunks; a.chunk = d->chunk;
+  a.chunk_base = 0;
   a.theta = (double)d->rope_theta; a.rope_mode = d->doc_rope_mode;
   a.Kbar = Kbar; a.Vbar = Vbar; a.KRbar = KRbar;
   return launch_pool(a, static_cast<hipStream_t>(stream));

@@ -17,6 +17,13 @@ namespace msa {
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 int hip_fail(hipError_t e, const char* what);
+// Argument checks shared by the entry points (msa_api.hip).
+int check_dims(const msa_dims* d);
+// K̄/V̄ pointer → device-visible address: device memory as is, pinned host
+// memory (on_host = 1) to its mapping; anything else is MSA_ERR_INVALID_ARG.
+int resolve_kv(const void* p, int on_host, const void** out, const char* name);
+// Same, with the memory kind read from the pointer.
+int resolve_any(const void* p, const void** out, const char* name);
 
 #define MSA_HIP(expr)                                   \
   do {                                                  \
@@ -163,6 +170,9 @@ struct PoolArgs {
   const uint16_t* K; const uint16_t* V; const uint16_t* KR;
   const int64_t* dto; const int64_t* dco;
   int32_t n_docs; int64_t n_tokens; int64_t n_chunks; int32_t chunk;
+  // chunk index of the first document's first chunk: the offsets in dco are
+  // absolute store rows, the outputs are written at those rows
+  int64_t chunk_base;
   double theta; int32_t rope_mode;
   uint16_t* Kbar; uint16_t* Vbar; uint16_t* KRbar;
   // filled by launch_pool (fp64, host): one-step rotations per frequency m

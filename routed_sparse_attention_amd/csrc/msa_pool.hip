@@ -95,9 +95,10 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a, int32_t first_ten
   const uint16_t* src = tensor == 0 ? a.K : (tensor == 1 ? a.V : a.KR);
   uint16_t* dst = tensor == 0 ? a.Kbar : (tensor == 1 ? a.Vbar : a.KRbar);
   if (dst == nullptr) return;
-  const int64_t c_begin = ((int64_t)blockIdx.x * kWavesPerWG + wave) * kChunksPerWave;
-  if (c_begin >= a.n_chunks) return;
-  const int64_t c_end = min(c_begin + (int64_t)kChunksPerWave, a.n_chunks);
+  const int64_t c_first = ((int64_t)blockIdx.x * kWavesPerWG + wave) * kChunksPerWave;
+  if (c_first >= a.n_chunks) return;
+  const int64_t c_begin = a.chunk_base + c_first;
+  const int64_t c_end = a.chunk_base + min(c_first + (int64_t)kChunksPerWave, a.n_chunks);
   const bool tok_rope = ROPE && a.rope_mode == MSA_DOC_ROPE_TOKEN;
   const bool chunk_rope = ROPE && a.rope_mode == MSA_DOC_ROPE_CHUNK;
 

@@ -5,6 +5,7 @@ every validation case below fails before anything is enqueued."""
 import ctypes
 import os
 import re
+import struct
 
 import numpy as np
 import pytest
@@ -29,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = msa.lib()
     for name in _declared():
         assert hasattr(L, name), f"libmsa.so does not export {name}"
-    assert L.msa_abi_version() == 2
+    assert L.msa_abi_version() == 3
 
 
 def test_default_dims_follow_the_pages():
@@ -91,3 +92,71 @@ def test_workspace_sizes():
     assert a >= 1_562_500 * 4 and b >= 64 * 250_000 * 4
     assert msa.sparse_attend_workspace(1, 129, 1024, d) > 0
     assert msa.lib().msa_route_topk_workspace(ctypes.byref(d), 0, 1, 10, 2) == 0
+
+
+def _header(n_docs=3, chunk=64, n_chunks=7, heads=8, head_dim=128, mask=7, magic=b"MSASTOR1",
+            version=1, hbytes=64):
+    return struct.pack("<8sIIiiqiiIif12x", magic, version, hbytes, n_docs, chunk, n_chunks, heads,
+                       head_dim, mask, 0, 1e6)
+
+
+def test_store_header_layout_is_64_bytes():
+    assert len(_header()) == 64
+
+
+def test_store_file_info_reads_the_header(tmp_path):
+    f = tmp_path / "ok.msastore"
+    f.write_bytes(_header(n_docs=5, n_chunks=11, mask=5) + bytes(48))
+    assert msa.store_file_info(str(f)) == (5, 11, 5)
+
+
+@pytest.mark.parametrize("kw,why", [
+    (dict(magic=b"NOTSTORE"), "bad magic"),
+    (dict(version=2), "unsupported version"),
+    (dict(hbytes=80), "unsupported version"),
+    (dict(n_docs=4, n_chunks=3), "malformed"),
+    (dict(mask=9), "malformed"),
+    (dict(chunk=0), "malformed"),
+])
+def test_store_file_info_rejects_malformed_headers(tmp_path, kw, why):
+    f = tmp_path / "bad.msastore"
+    f.write_bytes(_header(**kw))
+    with pytest.raises(msa.MsaError) as e:
+        msa.store_file_info(str(f))
+    assert e.value.code == -6 and why in str(e.value)
+
+
+def test_store_file_info_io_errors(tmp_path):
+    with pytest.raises(msa.MsaError) as e:
+        msa.store_file_info(str(tmp_path / "missing"))
+    assert e.value.code == -6
+    f = tmp_path / "short"
+    f.write_bytes(_header()[:40])
+    with pytest.raises(msa.MsaError) as e:
+        msa.store_file_info(str(f))
+    assert e.value.code == -6 and "header" in str(e.value)
+
+
+def test_store_validation_before_any_gpu_work():
+    """Store calls reject bad arguments before touching the GPU."""
+    L = msa.lib()
+    d = msa.dims()
+    dco_h = (ctypes.c_int64 * 5)(0, 2, 5, 0, 0)
+    st = msa._lib.StoreC(None, None, None, 16, ctypes.addressof(dco_h), 10, 4, 2, 5)
+    dto_h = (ctypes.c_int64 * 3)(0, 100, 180)
+    p = ctypes.c_void_p(16)
+    # one 700-token document is 11 chunks; the store has room for 10 - 5
+    big = (ctypes.c_int64 * 2)(0, 700)
+    rc = L.msa_store_append(ctypes.byref(d), ctypes.byref(st), p, p, p, p, big, 1, 700, None)
+    assert rc == -2 and b"do not fit" in L.msa_last_error() and st.n_docs == 2
+    rc = L.msa_store_append(ctypes.byref(d), ctypes.byref(st), p, p, p, p, dto_h, 2, 999, None)
+    assert rc == -2 and b"run from 0" in L.msa_last_error()
+    bad = (ctypes.c_int64 * 3)(0, 100, 100)
+    rc = L.msa_store_append(ctypes.byref(d), ctypes.byref(st), p, p, p, p, bad, 2, 100, None)
+    assert rc == -2 and b"document 1" in L.msa_last_error()
+    st.n_chunks = 4   # mirror ends at 5: inconsistent fill
+    rc = L.msa_store_append(ctypes.byref(d), ctypes.byref(st), p, p, p, p, dto_h, 2, 180, None)
+    assert rc == -2 and b"not at n_chunks" in L.msa_last_error()
+    st.n_chunks = 5
+    rc = L.msa_store_save(ctypes.byref(d), ctypes.byref(st), b"/tmp/x", None, 0)
+    assert rc == -1 and b"staging" in L.msa_last_error()
