@@ -17,11 +17,14 @@
 //             rows (and n_mem); the other blocks rotate Q and K_loc into the
 //             workspace (bf16), one thread per rotation pair;
 //   attn      flash attention, one wave per (32 query rows of one KV group,
-//             KV head, key split). Each 32-key tile of K and V is read with
-//             one 256-byte row per 16 lanes (coalesced, and large PCIe reads
-//             when K̄/V̄ sit in pinned host memory — they are read in place,
-//             with no staging copy) and staged in LDS: K row-major, V
-//             transposed, so both MFMA B fragments are 16-byte LDS reads.
+//             KV head, key split), about 2048 waves. Each 32-key tile of K
+//             and V is read with one 256-byte row per 16 lanes (coalesced,
+//             and large PCIe reads when K̄/V̄ sit in pinned host memory —
+//             they are read in place, with no staging copy) and staged in
+//             LDS: K row-major, V transposed (a lane holds 8 consecutive keys,
+//             so each dim's keys go out as one 16-byte store), so both MFMA B
+//             fragments are 16-byte LDS reads. Row maxima and sums use DPP
+//             within 16-lane rows and one exchange between rows.
 //             S = Q·K^T and O += P·V use v_mfma_f32_32x32x16_bf16; the online
 //             softmax runs in fp32 in the exp2 domain; P is re-laid out from
 //             the accumulator layout to the A-operand layout through LDS;
@@ -175,15 +178,10 @@ __global__ __launch_bounds__(64) void attn_kernel(const uint16_t* __restrict__ Q
       for (int ks = 0; ks < 8; ++ks) qa[ks] = make_uint4(0, 0, 0, 0);
     }
   }
-  // accumulator rows held by this lane: i(v) = 8(v/4) + 4·half + v%4
-  int u_of[16];
-  bool row_ok[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int r = rb * kRowTile + 8 * (v >> 2) + 4 * half + (v & 3);
-    row_ok[v] = r < rows_g;
-    u_of[v] = r / G;
-  }
+  // Accumulator rows held by this lane: r(v) = base_r + off(v), with
+  // off(v) = 8(v/4) + v%4 a constant; row r is valid while off(v) < rem.
+  const int base_r = rb * kRowTile + 4 * half;
+  const int rem = rows_g - base_r;
 
   f32x16_t O[4];
 #pragma unroll
@@ -194,34 +192,42 @@ __global__ __launch_bounds__(64) void attn_kernel(const uint16_t* __restrict__ Q
 #pragma unroll
   for (int v = 0; v < 16; ++v) { mrow[v] = -INFINITY; lpart[v] = 0.0f; }
 
-  const int sub = lane >> 4;       // row of a 4-row load group
-  const int dv = lane & 15;        // 16-byte vector within a 256-byte head row
+  // Load layout: lane (sub, dv) = (lane / 16, lane % 16) reads the 16-byte
+  // vector dv of keys 8·sub .. 8·sub + 7 (one instruction covers 4 keys' 256-byte
+  // head rows, 16 lanes each), so a lane holds 8 consecutive keys of the same
+  // 8 dims and writes each dim's 8 keys of V^T as one 16-byte store.
+  const int sub = lane >> 4;
+  const int dv = lane & 15;
   for (int kt = k_begin; kt < k_end; kt += kKeyTile) {
-    // ---- K and V tiles: 16 lanes per 256-byte row, 4 rows per instruction
+    // ---- K and V tiles. Keys past the split are clamped to its last key (a
+    //      real row, so finite) and masked out of the softmax below.
     uint4 kx[8], vx[8];
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
-      const int j = kt + it * 4 + sub;
-      kx[it] = vx[it] = make_uint4(0, 0, 0, 0);
-      if (j < k_end) {
-        const int64_t off = j < n_mem ? ((int64_t)mem_rows[j] * kHeads + g) * kDim
-                                      : ((int64_t)(j - n_mem) * kHeads + g) * kDim;
-        const uint16_t* kb = j < n_mem ? Kbar : Kloc;
-        const uint16_t* vb = j < n_mem ? Vbar : Vloc;
-        kx[it] = reinterpret_cast<const uint4*>(kb + off)[dv];
-        vx[it] = reinterpret_cast<const uint4*>(vb + off)[dv];
-      }
+      const int j = min(kt + sub * 8 + it, k_end - 1);
+      const bool mem = j < n_mem;
+      const int64_t off = mem ? ((int64_t)mem_rows[j] * kHeads + g) * kDim
+                              : ((int64_t)(j - n_mem) * kHeads + g) * kDim;
+      kx[it] = reinterpret_cast<const uint4*>((mem ? Kbar : Kloc) + off)[dv];
+      vx[it] = reinterpret_cast<const uint4*>((mem ? Vbar : Vloc) + off)[dv];
     }
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int kk = it * 4 + sub;
-      *reinterpret_cast<uint4*>(&Ks[kk * kKPitch + dv * 8]) = kx[it];
-      const uint32_t w[4] = {vx[it].x, vx[it].y, vx[it].z, vx[it].w};
+    for (int it = 0; it < 8; ++it)
+      *reinterpret_cast<uint4*>(&Ks[(sub * 8 + it) * kKPitch + dv * 8]) = kx[it];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(dv * 8 + 2 * e) * kVPitch + kk] = (uint16_t)(w[e] & 0xffffu);
-        Vt[(dv * 8 + 2 * e + 1) * kVPitch + kk] = (uint16_t)(w[e] >> 16);
+    for (int e = 0; e < 8; ++e) {
+      // dim dv·8 + e of keys 8·sub .. 8·sub + 7
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4& a = vx[2 * q];
+        const uint4& b = vx[2 * q + 1];
+        const uint32_t wa = (e >> 1) == 0 ? a.x : (e >> 1) == 1 ? a.y : (e >> 1) == 2 ? a.z : a.w;
+        const uint32_t wb = (e >> 1) == 0 ? b.x : (e >> 1) == 1 ? b.y : (e >> 1) == 2 ? b.z : b.w;
+        w[q] = (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
       }
+      *reinterpret_cast<uint4*>(&Vt[(dv * 8 + e) * kVPitch + sub * 8]) =
+          make_uint4(w[0], w[1], w[2], w[3]);
     }
     __syncthreads();
 
@@ -238,17 +244,22 @@ __global__ __launch_bounds__(64) void attn_kernel(const uint16_t* __restrict__ Q
     // ---- mask, scale to the log2 domain, online softmax
     const int j = kt + col;
     const bool key_ok = j < k_end;
-    const int vloc = j - n_mem;
+    // causal: local key vloc is visible to query token u = r / G iff
+    // u >= vloc - (M_loc - M), i.e. r >= (vloc - (M_loc - M))·G
+    const int lim_off = j < n_mem ? -(1 << 30) : (j - n_mem - (M_loc - M)) * G - base_r;
     float p[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const bool ok = key_ok && row_ok[v] && (j < n_mem || vloc <= (M_loc - M) + u_of[v]);
+      const int off = 8 * (v >> 2) + (v & 3);
+      const bool ok = key_ok && off < rem && off >= lim_off;
       const float s = ok ? S[v] * qk_scale_log2 : -INFINITY;
+      // max over the row's 32 key lanes: four DPP steps within each 16-lane
+      // row, then one exchange between the two rows of this half
       float t = s;
-      t = fmaxf(t, __shfl_xor(t, 1));
-      t = fmaxf(t, __shfl_xor(t, 2));
-      t = fmaxf(t, __shfl_xor(t, 4));
-      t = fmaxf(t, __shfl_xor(t, 8));
+      t = fmaxf(t, dpp_f<0xB1>(t));    // quad_perm [1,0,3,2]
+      t = fmaxf(t, dpp_f<0x4E>(t));    // quad_perm [2,3,0,1]
+      t = fmaxf(t, dpp_f<0x141>(t));   // row_half_mirror
+      t = fmaxf(t, dpp_f<0x140>(t));   // row_mirror
       t = fmaxf(t, __shfl_xor(t, 16));
       const float mn = fmaxf(mrow[v], t);
       const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(mrow[v] - mn);
@@ -286,18 +297,15 @@ __global__ __launch_bounds__(64) void attn_kernel(const uint16_t* __restrict__ Q
   // ---- row sums of p over the 32 key lanes, then write the partials
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    float t = lpart[v];
-    t += __shfl_xor(t, 1);
-    t += __shfl_xor(t, 2);
-    t += __shfl_xor(t, 4);
-    t += __shfl_xor(t, 8);
+    float t = row_sum16(lpart[v]);
     t += __shfl_xor(t, 16);
     lpart[v] = t;
   }
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    if (!row_ok[v]) continue;
-    const int r = rb * kRowTile + 8 * (v >> 2) + 4 * half + (v & 3);
+    const int off = 8 * (v >> 2) + (v & 3);
+    if (off >= rem) continue;
+    const int r = base_r + off;
     const int u = r / G, h = g * G + r % G;
     const int64_t grow = (int64_t)split * n_rows_tot + (int64_t)u * Hq + h;
 #pragma unroll
@@ -360,8 +368,9 @@ AttnPlan attn_plan(int32_t M, int32_t M_loc, int32_t Hq, int64_t max_sel) {
   const int32_t G = Hq / kHeads;
   p.row_blocks = (M * G + kRowTile - 1) / kRowTile;
   const int64_t max_keys = max_sel + M_loc;
-  // aim for >= 512 waves in flight across the chip, at most kMaxSplits splits
-  int64_t want = 512 / ((int64_t)p.row_blocks * kHeads);
+  // aim for >= 2048 waves (8 per CU: one tile's loads of each in flight while
+  // the others compute), at most kMaxSplits splits
+  int64_t want = 2048 / ((int64_t)p.row_blocks * kHeads);
   if (want < 1) want = 1;
   const int64_t tiles = (max_keys + kKeyTile - 1) / kKeyTile;
   int64_t tiles_per_split = (tiles + want - 1) / want;
@@ -371,13 +380,20 @@ AttnPlan attn_plan(int32_t M, int32_t M_loc, int32_t Hq, int64_t max_sel) {
   p.key_split = (int32_t)(tiles_per_split * kKeyTile);
   p.n_splits = (int32_t)((max_keys + p.key_split - 1) / p.key_split);
   if (p.n_splits < 1) p.n_splits = 1;
+  // The partials are sized for the most splits any key count up to max_keys
+  // can produce: ceil(t / ceil(t / want)) <= want, and <= t, and <= kMaxSplits.
+  // (The split count is not monotonic in t, and a workspace sized at the
+  // capacity is reused for smaller contexts, e.g. across interleave rounds.)
+  int64_t ws_splits = want < kMaxSplits ? want : kMaxSplits;
+  if (ws_splits > tiles) ws_splits = tiles;
+  if (ws_splits < p.n_splits) ws_splits = p.n_splits;
   size_t o = 0;
   p.off_rows = o; o = align_up(o + sizeof(int32_t) * (size_t)(max_sel > 0 ? max_sel : 1), 256);
   p.off_nmem = o; o = align_up(o + sizeof(int32_t), 256);
   p.off_qr = o; o = align_up(o + 2 * (size_t)M * Hq * kDim, 256);
   p.off_kr = o; o = align_up(o + 2 * (size_t)M_loc * kHeads * kDim, 256);
-  p.off_opart = o; o = align_up(o + 4 * (size_t)p.n_splits * M * Hq * kDim, 256);
-  p.off_ml = o; o = align_up(o + 4 * 2 * (size_t)p.n_splits * M * Hq, 256);
+  p.off_opart = o; o = align_up(o + 4 * (size_t)ws_splits * M * Hq * kDim, 256);
+  p.off_ml = o; o = align_up(o + 4 * 2 * (size_t)ws_splits * M * Hq, 256);
   p.total = o;
   return p;
 }

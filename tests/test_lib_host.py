@@ -160,3 +160,18 @@ def test_store_validation_before_any_gpu_work():
     st.n_chunks = 5
     rc = L.msa_store_save(ctypes.byref(d), ctypes.byref(st), b"/tmp/x", None, 0)
     assert rc == -1 and b"staging" in L.msa_last_error()
+
+
+def test_attend_workspace_covers_every_smaller_context():
+    """A workspace sized for cap_loc local tokens serves every smaller context
+    (interleave rounds reuse one): the size is monotone in M_loc."""
+    d = msa.dims()
+    for M in (1, 8, 64, 256):
+        for max_sel in (16, 1024, 2048):
+            cap = 3 * 256 + M
+            top = msa.sparse_attend_workspace(M, cap, max_sel, d)
+            prev = 0
+            for M_loc in range(M, cap + 1, 7):
+                w = msa.sparse_attend_workspace(M, M_loc, max_sel, d)
+                assert prev <= w <= top, (M, max_sel, M_loc)
+                prev = w
