@@ -335,3 +335,94 @@ def store_bytes(n_tokens: int, chunk: int = CHUNK, heads: int = N_ROUTER_HEADS,
                 head_dim: int = HEAD_DIM, layers: int = N_ROUTED_LAYERS, bytes_per: int = 2) -> int:
     """Bytes of one pooled tensor (K̄, V̄ or K̄^R) over all routed layers."""
     return (n_tokens // chunk) * heads * head_dim * bytes_per * layers
+
+
+# ----------------------------------------------------------------------------
+# Router supervision: the auxiliary contrastive loss and its gradient
+# ([techblg] §M training-data bullet: L_aux = −(1/|P|) Σ_i log[ exp(s_i⁺/τ) /
+#  (exp(s_i⁺/τ) + Σ_j exp(s_ij⁻/τ)) ] supervises every layer's router; the
+#  temperature τ is fixed but its value is not given).
+# Readings: s are the query's routing document scores (step 6: max over a
+# document's chunks of the max over query tokens of the head-mean cosine); P
+# is the query's set of positive documents and the negatives of every
+# positive are all other documents of the store; τ is a parameter. Through
+# the two maxima the gradient reaches one (chunk, token) pair per document:
+# the first chunk (lowest index) attaining the document score and, in it, the
+# first token (lowest index) attaining the chunk score. A norm at or below the
+# clamp contributes x / eps, so its gradient is the plain k̂ / eps (or q̂ / eps).
+# ----------------------------------------------------------------------------
+def aux_loss_f64(q, k, doc_chunk_offsets, positives, tau: float, eps: float = NORM_EPS):
+    """One query on float64 arrays: q [M,H,D] (its router tokens), k [C,H,D]
+    (the pooled router keys). Returns (loss, dq [M,H,D], dk [C,H,D], s [N],
+    c_star [N], t_star [N], gaps [N]) where gaps[i] is the smaller of the
+    margins that fix c_star[i] and t_star[i] (inf where unique by size)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    dco = np.asarray(doc_chunk_offsets, dtype=np.int64)
+    M, H, _ = q.shape
+    N = len(dco) - 1
+    rq = np.sqrt((q * q).sum(axis=-1))                  # [M,H]
+    rk = np.sqrt((k * k).sum(axis=-1))                  # [C,H]
+    nq, nk = np.maximum(rq, eps), np.maximum(rk, eps)
+    qh, kh = q / nq[..., None], k / nk[..., None]
+    cos = np.einsum("mhd,chd->mch", qh, kh)              # [M,C,H]
+    S = cos.sum(axis=-1) / H                             # [M,C]
+    Sc = S.max(axis=0)                                   # [C]
+    s = np.empty(N)
+    c_star = np.empty(N, dtype=np.int64)
+    t_star = np.empty(N, dtype=np.int64)
+    gaps = np.full(N, np.inf)
+    for i in range(N):
+        seg = Sc[dco[i]:dco[i + 1]]
+        j = int(np.argmax(seg))                          # first maximum
+        c = int(dco[i]) + j
+        t = int(np.argmax(S[:, c]))                      # first maximum
+        s[i], c_star[i], t_star[i] = seg[j], c, t
+        if len(seg) > 1:
+            gaps[i] = min(gaps[i], seg[j] - np.max(np.delete(seg, j)))
+        if M > 1:
+            gaps[i] = min(gaps[i], S[t, c] - np.max(np.delete(S[:, c], t)))
+    P = sorted(set(int(x) for x in positives))
+    neg = np.ones(N, dtype=bool)
+    neg[P] = False
+    a = s / tau
+    e = np.exp(a - a.max())                              # shared shift
+    z_neg = e[neg].sum()
+    loss = 0.0
+    ds = np.zeros(N)
+    for i in P:
+        z = e[i] + z_neg
+        loss -= math.log(e[i] / z)
+        ds[i] -= (1.0 - e[i] / z) / tau
+        ds[neg] += e[neg] / z / tau
+    loss /= len(P)
+    ds /= len(P)
+    # chain rule: ds_i → the head-mean cosine at (t*, c*) → each head's cosine
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    for i in range(N):
+        g = ds[i] / H
+        c, t = c_star[i], t_star[i]
+        ch = cos[t, c]                                   # [H]
+        gq = np.where((rq[t] > eps)[:, None], kh[c] - ch[:, None] * qh[t], kh[c]) / nq[t][:, None]
+        gk = np.where((rk[c] > eps)[:, None], qh[t] - ch[:, None] * kh[c], qh[t]) / nk[c][:, None]
+        dq[t] += g * gq
+        dk[c] += g * gk
+    return loss, dq, dk, s, c_star, t_star, gaps
+
+
+def route_aux_loss(QR, KRbar, doc_chunk_offsets, positives, tau: float):
+    """B queries: QR [B,M,H,D] and KRbar [C,H,D] bf16 patterns, positives[b]
+    the positive document ids of query b. Returns (loss [B], dQR [B,M,H,D],
+    dKRbar [C,H,D] summed over the queries, s [B,N], c_star [B,N],
+    t_star [B,N], gaps [B,N])."""
+    QR = np.asarray(QR)
+    k = bf16_to_f64(KRbar)
+    B = QR.shape[0]
+    outs = [aux_loss_f64(bf16_to_f64(QR[b]), k, doc_chunk_offsets, positives[b], tau)
+            for b in range(B)]
+    loss = np.array([o[0] for o in outs])
+    dQ = np.stack([o[1] for o in outs])
+    dK = np.sum([o[2] for o in outs], axis=0)
+    return (loss, dQ, dK, np.stack([o[3] for o in outs]), np.stack([o[4] for o in outs]),
+            np.stack([o[5] for o in outs]), np.stack([o[6] for o in outs]))

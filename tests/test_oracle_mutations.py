@@ -47,6 +47,14 @@ MUTATIONS = {
                                    "    if True:\n        kl = rope_rotate"),
     "attend_values_from_keys": ("vals = np.concatenate([vmem[:, g, :], vl[:n_vis, g, :]], axis=0)",
                                 "vals = np.concatenate([kmem[:, g, :], vl[:n_vis, g, :]], axis=0)"),
+    "aux_no_projection": ("kh[c] - ch[:, None] * qh[t], kh[c])", "kh[c], kh[c])"),
+    "aux_key_grad_swapped": ("qh[t] - ch[:, None] * kh[c], qh[t])", "kh[c] - ch[:, None] * qh[t], qh[t])"),
+    "aux_negatives_include_positives": ("neg[P] = False", "neg[P] = True"),
+    "aux_missing_temperature": ("ds[neg] += e[neg] / z / tau", "ds[neg] += e[neg] / z"),
+    "aux_sum_not_mean": ("    loss /= len(P)\n    ds /= len(P)", "    pass"),
+    "aux_last_chunk_on_ties": ("j = int(np.argmax(seg))                          # first maximum",
+                               "j = len(seg) - 1 - int(np.argmax(seg[::-1]))"),
+    "aux_grad_not_divided_by_heads": ("g = ds[i] / H", "g = ds[i]"),
 }
 
 # fast pins first: the loop stops at the first pin that fails

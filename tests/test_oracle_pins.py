@@ -488,3 +488,106 @@ def test_interleave_incremental_equals_full_reroute():
             assert doc in set(ids)
             assert all(d in set(ids) for d in chain[:r + 1])
             assert out.shape == (96, 32, 128)
+
+
+# ---------------------------------------------------------------------------
+# Router supervision: L_aux and its gradient ([techblg] §M training bullet)
+# ---------------------------------------------------------------------------
+def _aux_instance(seed, M=3, counts=(2, 3, 4), scale=1.0):
+    rng = np.random.default_rng(seed)
+    dco = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    q = rng.normal(size=(M, 8, 128)) * scale
+    k = rng.normal(size=(int(dco[-1]), 8, 128))
+    return q, k, dco
+
+
+def test_aux_loss_gradient_matches_finite_differences():
+    """Central differences on sampled coordinates of q and k (the maxima are
+    attained with clear margins on random data, so the loss is smooth there)."""
+    q, k, dco = _aux_instance(11)
+    pos, tau = [1], 0.1
+    loss, dq, dk, s, cs, ts, gaps = O.aux_loss_f64(q, k, dco, pos, tau)
+    assert np.all(gaps > 1e-3)
+    rng = np.random.default_rng(12)
+    h = 1e-6
+    for arr, grad in ((q, dq), (k, dk)):
+        for _ in range(40):
+            idx = tuple(int(rng.integers(0, n)) for n in arr.shape)
+            old = arr[idx]
+            arr[idx] = old + h
+            fp = O.aux_loss_f64(q, k, dco, pos, tau)[0]
+            arr[idx] = old - h
+            fm = O.aux_loss_f64(q, k, dco, pos, tau)[0]
+            arr[idx] = old
+            fd = (fp - fm) / (2 * h)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (idx, fd, grad[idx])
+
+
+def test_aux_loss_gradient_matches_torch_autograd():
+    """An independent forward in torch (float64, CPU) differentiated by
+    autograd, including a query token at the norm clamp (a zero vector)."""
+    q, k, dco = _aux_instance(13, M=4, counts=(3, 1, 5, 2))
+    q[2, 5] = 0.0                       # clamped norm: the gradient is k̂ / eps
+    pos, tau = [0, 3], 0.05
+    loss, dq, dk, *_ = O.aux_loss_f64(q, k, dco, pos, tau)
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    qh = tq / tq.norm(dim=-1, keepdim=True).clamp_min(O.NORM_EPS)
+    kh = tk / tk.norm(dim=-1, keepdim=True).clamp_min(O.NORM_EPS)
+    S = torch.einsum("mhd,chd->mc", qh, kh) / 8
+    s = torch.stack([S[:, int(dco[i]):int(dco[i + 1])].max() for i in range(len(dco) - 1)])
+    neg = torch.ones(len(s), dtype=torch.bool)
+    neg[pos] = False
+    terms = []
+    for i in pos:
+        logits = torch.cat([(s[i] / tau).reshape(1), s[neg] / tau])
+        terms.append(-(logits[0] - torch.logsumexp(logits, 0)))
+    L = torch.stack(terms).mean()
+    L.backward()
+    assert abs(L.item() - loss) < 1e-12
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-9, atol=1e-12)
+
+
+def test_aux_loss_invariants():
+    q, k, dco = _aux_instance(14, M=2, counts=(4, 4, 4, 4))
+    pos, tau = [2], 0.2
+    loss, dq, dk, *_ = O.aux_loss_f64(q, k, dco, pos, tau)
+    # cosines ignore scale: each row's gradient is orthogonal to the row
+    assert np.abs((dq * q).sum(-1)).max() < 1e-12
+    assert np.abs((dk * k).sum(-1)).max() < 1e-12
+    # ... and scaling q by 3 keeps the loss and divides dq by 3
+    l3, dq3, dk3, *_ = O.aux_loss_f64(3.0 * q, k, dco, pos, tau)
+    assert abs(l3 - loss) < 1e-12
+    np.testing.assert_allclose(dq3, dq / 3.0, rtol=1e-9, atol=1e-15)
+    np.testing.assert_allclose(dk3, dk, rtol=1e-9, atol=1e-15)
+
+
+def test_aux_loss_closed_forms():
+    rng = np.random.default_rng(15)
+    q = rng.normal(size=(2, 8, 128))
+    row = rng.normal(size=(8, 128))
+    k = np.repeat(row[None], 6, axis=0)            # every chunk the same key
+    dco = np.array([0, 1, 3, 4, 6])
+    # all document scores equal: each positive's share is 1 / (1 + n_neg)
+    for pos in ([0], [1, 3]):
+        loss = O.aux_loss_f64(q, k, dco, pos, 0.07)[0]
+        assert abs(loss - math.log(4 - len(pos) + 1)) < 1e-12
+    # no negatives: every positive has probability 1, loss and gradients 0
+    loss, dq, dk, *_ = O.aux_loss_f64(q, k, dco, [0, 1, 2, 3], 0.07)
+    assert abs(loss) < 1e-15 and not dq.any() and not dk.any()
+    # very high temperature: the scores stop mattering
+    q2, k2, dco2 = _aux_instance(16, counts=(2, 2, 2, 2, 2))
+    assert abs(O.aux_loss_f64(q2, k2, dco2, [4], 1e12)[0] - math.log(5)) < 1e-9
+
+
+def test_aux_loss_subgradient_rules():
+    """Ties at the maxima go to the first chunk and the first token."""
+    rng = np.random.default_rng(17)
+    u = rng.normal(size=(8, 128))
+    q = np.stack([u, u, rng.normal(size=(8, 128))])   # tokens 0 and 1 identical
+    k = np.stack([rng.normal(size=(8, 128)), u, u, rng.normal(size=(8, 128))])
+    dco = np.array([0, 3, 4])                           # doc 0: chunks 0-2 (1 and 2 tie)
+    _, dq, dk, s, cs, ts, gaps = O.aux_loss_f64(q, k, dco, [1], 0.1)
+    assert cs[0] == 1 and ts[0] == 0 and gaps[0] == 0.0
+    assert not dk[2].any() and not dq[1].any()
