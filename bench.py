@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", choices=["100m", "route16m", "pool10m", "interleave", "store",
-                                           "copy"],
+                                           "aux", "copy"],
                     default="100m")
     ap.add_argument("--layers", type=int, default=18)
     ap.add_argument("--chunks", type=int, default=1_562_500)
@@ -634,6 +634,58 @@ def workload_store(args):
     return r
 
 
+# ---------------------------------------------------------------------------
+# aux: router supervision — L_aux and its gradient on the 16M-token store
+# ---------------------------------------------------------------------------
+def workload_aux(args):
+    import torch
+
+    import routed_sparse_attention_amd as msa
+    import synth
+
+    dev = "cuda"
+    store, q = synth.cfg3_batched(dev)
+    B, C, N = q.QR.shape[0], store.n_chunks, store.n_docs
+    d = msa.dims()
+    dco = torch.from_numpy(store.doc_chunk_offsets).to(dev)
+    tau = 0.05
+    positives = [list(p) for p in q.planted_docs]
+    need = msa.lib().msa_route_aux_loss_workspace(ctypes.byref(d), B, 1, C, N)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    loss, dQ, dK, ds, bc, bt = msa.route_aux_loss(q.QR, store.KRbar, dco, positives, tau, d, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(loss).all() and torch.isfinite(dQ).all() and torch.isfinite(dK).all()
+
+    def step(tm):
+        e0 = tm.ev() if tm else None
+        msa.route_aux_loss(q.QR, store.KRbar, dco, positives, tau, d, ws=ws)
+        if tm:
+            tm.add("aux", e0, tm.ev())
+
+    tm = Timer()
+    ms = run_timed(args, step, tm)
+    tokens = C * TOKENS_PER_CHUNK
+    # algorithmic bytes: the routing scan (router keys once, scores written),
+    # dK̄^R written once (fp32), and per (query, document) the chosen key row
+    # and query row read back (bf16) by the backward
+    nbytes = C * ROW_BYTES + B * C * 4 + C * ROW_BYTES * 2 + B * N * 2 * ROW_BYTES
+    achieved = nbytes / (tm.avg_us("aux") * 1e-6) / 1e9
+    r = base_result(args, "memory tokens supervised/sec per query", B * tokens / (ms * 1e-3),
+                    "tokens/s", ms,
+                    {"workload": f"router auxiliary loss + gradient: {B} single-token queries, "
+                                 f"2 positives each, tau {tau}, over a {tokens / 1e6:.0f}M-token "
+                                 f"store ({N:,} documents)",
+                     "queries": B, "chunks": C, "documents": N, "tau": tau})
+    r.update({"aux_us": tm.avg_us("aux"), "aux_stats": tm.stats("aux"),
+              "mean_loss": float(loss.mean().item()),
+              "roofline": {"bound": "hbm", "kernel": "msa_route_aux_loss (scan + backward kernels)",
+                           "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                           "bytes_per_launch": nbytes},
+              "cpu_baseline": None})
+    return r
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -645,7 +697,7 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     fn = {"100m": workload_100m, "route16m": workload_route16m, "pool10m": workload_pool10m,
-          "store": workload_store,
+          "store": workload_store, "aux": workload_aux,
           "interleave": workload_interleave, "copy": workload_copy}[args.workload]
     print(json.dumps(fn(args)), flush=True)
 

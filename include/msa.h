@@ -99,7 +99,7 @@ const char* msa_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
 int32_t msa_abi_version(void);
-#define MSA_ABI_VERSION 3
+#define MSA_ABI_VERSION 4
 
 /* ------------------------------------------------------------------------ */
 /* Chunk plan (host, pure). Each document is cut into ceil(n_i / chunk)
@@ -249,6 +249,42 @@ int32_t msa_interleave_step(const msa_dims* d, msa_interleave_state* st, const m
                             const int64_t* doc_chunk_offsets, int32_t n_docs,
                             int64_t max_sel_chunks, msa_bf16* out, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Router supervision: the auxiliary contrastive loss of the pages and its
+ * gradient (techblg section M, training bullet: L_aux = −(1/|P|) Σ_i log[
+ * exp(s_i⁺/τ) / (exp(s_i⁺/τ) + Σ_j exp(s_ij⁻/τ)) ], applied to every routed
+ * layer; τ fixed, its value not given). Readings: s are the query's routing
+ * document scores (max over a document's chunks of the max over query tokens
+ * of the head-mean cosine); the negatives of every positive are all other
+ * documents of the store; τ is a parameter; through the two maxima the
+ * gradient reaches one (chunk, token) pair per document — the first chunk
+ * attaining the document score (by the routing scan's chunk scores) and, in
+ * it, the first token attaining the chunk score (recomputed in fp32, which
+ * also gives the s used in the loss).
+ *   QR [B, M, n_router_heads, 128] bf16; KRbar [n_chunks, n_router_heads, 128]
+ *     bf16; doc_chunk_offsets [n_docs+1] (device).
+ *   pos_ids [B, max_pos] int32, n_pos [B] int32 (device): query b's positives
+ *     are pos_ids[b][0 .. n_pos[b]); ids outside [0, n_docs) are ignored and
+ *     repeats count once; a query with no valid positive gets loss 0 and no
+ *     gradient.
+ *   tau > 0 (MSA_ERR_INVALID_ARG otherwise). token_reduce must be MAX
+ *     (MEAN is MSA_ERR_UNSUPPORTED).
+ *   loss [B] fp32 (written). dQR [B, M, n_router_heads, 128] fp32 and dKRbar
+ *     [n_chunks, n_router_heads, 128] fp32 (written densely: rows without
+ *     gradient are 0; dKRbar sums over the B queries). doc_scores [B, n_docs]
+ *     fp32 (written; may be NULL). best_chunk, best_token [B, n_docs] int32
+ *     (written; may be NULL): the (chunk, token) pair each document's
+ *     gradient went to. Only chunks inside a document are written in dKRbar.
+ *   Results are deterministic (fixed reduction orders, no atomics). */
+size_t msa_route_aux_loss_workspace(const msa_dims* d, int32_t B, int32_t M, int64_t n_chunks,
+                                    int32_t n_docs);
+int32_t msa_route_aux_loss(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
+                           const msa_bf16* KRbar, const int64_t* doc_chunk_offsets,
+                           int32_t n_docs, int64_t n_chunks, const int32_t* pos_ids,
+                           const int32_t* n_pos, int32_t max_pos, float tau, float* loss,
+                           float* dQR, float* dKRbar, float* doc_scores, int32_t* best_chunk,
+                           int32_t* best_token, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Streaming memory update: a pooled store that grows by whole documents

@@ -351,11 +351,15 @@ def store_bytes(n_tokens: int, chunk: int = CHUNK, heads: int = N_ROUTER_HEADS,
 # first token (lowest index) attaining the chunk score. A norm at or below the
 # clamp contributes x / eps, so its gradient is the plain k̂ / eps (or q̂ / eps).
 # ----------------------------------------------------------------------------
-def aux_loss_f64(q, k, doc_chunk_offsets, positives, tau: float, eps: float = NORM_EPS):
+def aux_loss_f64(q, k, doc_chunk_offsets, positives, tau: float, eps: float = NORM_EPS,
+                 choice=None):
     """One query on float64 arrays: q [M,H,D] (its router tokens), k [C,H,D]
     (the pooled router keys). Returns (loss, dq [M,H,D], dk [C,H,D], s [N],
     c_star [N], t_star [N], gaps [N]) where gaps[i] is the smaller of the
-    margins that fix c_star[i] and t_star[i] (inf where unique by size)."""
+    margins that fix c_star[i] and t_star[i] (inf where unique by size).
+    ``choice`` = (c_star, t_star) evaluates the loss and gradient at given
+    (chunk, token) pairs instead of the first maxima (s_i is then the score
+    at that pair) — another element of the subgradient where maxima tie."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     dco = np.asarray(doc_chunk_offsets, dtype=np.int64)
@@ -377,7 +381,9 @@ def aux_loss_f64(q, k, doc_chunk_offsets, positives, tau: float, eps: float = NO
         j = int(np.argmax(seg))                          # first maximum
         c = int(dco[i]) + j
         t = int(np.argmax(S[:, c]))                      # first maximum
-        s[i], c_star[i], t_star[i] = seg[j], c, t
+        if choice is not None:
+            c, t = int(choice[0][i]), int(choice[1][i])
+        s[i], c_star[i], t_star[i] = S[t, c], c, t
         if len(seg) > 1:
             gaps[i] = min(gaps[i], seg[j] - np.max(np.delete(seg, j)))
         if M > 1:
@@ -411,15 +417,17 @@ def aux_loss_f64(q, k, doc_chunk_offsets, positives, tau: float, eps: float = NO
     return loss, dq, dk, s, c_star, t_star, gaps
 
 
-def route_aux_loss(QR, KRbar, doc_chunk_offsets, positives, tau: float):
+def route_aux_loss(QR, KRbar, doc_chunk_offsets, positives, tau: float, choice=None):
     """B queries: QR [B,M,H,D] and KRbar [C,H,D] bf16 patterns, positives[b]
-    the positive document ids of query b. Returns (loss [B], dQR [B,M,H,D],
+    the positive document ids of query b (``choice`` = (c_star [B,N],
+    t_star [B,N]) as in aux_loss_f64). Returns (loss [B], dQR [B,M,H,D],
     dKRbar [C,H,D] summed over the queries, s [B,N], c_star [B,N],
     t_star [B,N], gaps [B,N])."""
     QR = np.asarray(QR)
     k = bf16_to_f64(KRbar)
     B = QR.shape[0]
-    outs = [aux_loss_f64(bf16_to_f64(QR[b]), k, doc_chunk_offsets, positives[b], tau)
+    outs = [aux_loss_f64(bf16_to_f64(QR[b]), k, doc_chunk_offsets, positives[b], tau,
+                         choice=None if choice is None else (choice[0][b], choice[1][b]))
             for b in range(B)]
     loss = np.array([o[0] for o in outs])
     dQ = np.stack([o[1] for o in outs])

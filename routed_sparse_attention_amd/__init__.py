@@ -5,11 +5,12 @@ The compute lives in ``libmsa.so`` (hand-written HIP for gfx950, C ABI in
 ``encode_pool`` (chunk mean-pooling with document RoPE), ``route_topk``
 (cosine routing, document max, top-k), ``sparse_attend`` (assembly, global
 RoPE, GQA attention), ``Interleave`` (Memory Interleave rounds) and
-``Store`` (a pooled store that grows by whole documents, with save/load).
+``Store`` (a pooled store that grows by whole documents, with save/load) and
+``route_aux_loss`` (the router's auxiliary contrastive loss and its gradient).
 """
 from ._lib import (  # noqa: F401
     DOC_ROPE_CHUNK, DOC_ROPE_TOKEN, EXPORTED, LIB_PATH, STORE_K, STORE_KR, STORE_V,
     TOKEN_REDUCE_MAX, TOKEN_REDUCE_MEAN, Dims, Interleave, MsaError, Store, dims, encode_pool,
-    lib, plan_chunks, route_topk, route_scores, route_topk_workspace, select_topk, sparse_attend,
+    lib, plan_chunks, route_aux_loss, route_topk, route_scores, route_topk_workspace, select_topk, sparse_attend,
     sparse_attend_workspace, store_file_info,
 )

@@ -29,7 +29,8 @@ EXPORTED = [
     "msa_route_scores_workspace", "msa_route_scores", "msa_select_topk_workspace", "msa_select_topk",
     "msa_sparse_attend_workspace", "msa_sparse_attend", "msa_interleave_reset",
     "msa_interleave_step_workspace", "msa_interleave_step", "msa_store_reset", "msa_store_append",
-    "msa_store_save", "msa_store_load", "msa_store_file_info",
+    "msa_store_save", "msa_store_load", "msa_store_file_info", "msa_route_aux_loss_workspace",
+    "msa_route_aux_loss",
 ]
 STORE_KR, STORE_K, STORE_V = 1, 2, 4   # tensor bits of a store file
 
@@ -108,6 +109,9 @@ def lib() -> ctypes.CDLL:
         "msa_store_load": (_i32, [_DP, ctypes.POINTER(StoreC), ctypes.c_char_p, _vp, _sz]),
         "msa_store_file_info": (_i32, [ctypes.c_char_p, ctypes.POINTER(_i32), ctypes.POINTER(_i64),
                                        ctypes.POINTER(ctypes.c_uint32)]),
+        "msa_route_aux_loss_workspace": (_sz, [_DP, _i32, _i32, _i64, _i32]),
+        "msa_route_aux_loss": (_i32, [_DP, _vp, _i32, _i32, _vp, _vp, _i32, _i64, _vp, _vp, _i32,
+                                      ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -459,3 +463,40 @@ class Store:
         stg = self._staging(staging_bytes)
         _check(lib().msa_store_load(ctypes.byref(self.d), ctypes.byref(self.st), os.fsencode(path),
                                     _p(stg), stg.numel()))
+
+
+# ---------------------------------------------------------------------------
+def route_aux_loss(QR, KRbar, doc_chunk_offsets, positives, tau: float, d: Dims | None = None,
+                   ws=None):
+    """The router's auxiliary contrastive loss and its gradient for B queries
+    (msa_route_aux_loss). ``positives[b]`` lists query b's positive document
+    ids. Returns (loss [B], dQR [B,M,8,128], dKRbar [C,8,128], doc_scores
+    [B,N], best_chunk [B,N], best_token [B,N])."""
+    d = d or dims()
+    _need(QR, "QR", torch.bfloat16, ndim=4)
+    _need(KRbar, "KRbar", torch.bfloat16, ndim=3)
+    _need(doc_chunk_offsets, "doc_chunk_offsets", torch.int64)
+    B, M, C = QR.shape[0], QR.shape[1], KRbar.shape[0]
+    N = doc_chunk_offsets.numel() - 1
+    dev = QR.device
+    max_pos = max(1, max(len(p) for p in positives))
+    pos = torch.full((B, max_pos), -1, dtype=torch.int32)
+    for b, p in enumerate(positives):
+        if len(p):
+            pos[b, :len(p)] = torch.tensor(list(p), dtype=torch.int32)
+    pos = pos.to(dev)
+    n_pos = torch.tensor([len(p) for p in positives], dtype=torch.int32, device=dev)
+    loss = torch.empty((B,), dtype=torch.float32, device=dev)
+    dQR = torch.empty((B, M, 8, 128), dtype=torch.float32, device=dev)
+    dKR = torch.empty((C, 8, 128), dtype=torch.float32, device=dev)
+    ds = torch.empty((B, N), dtype=torch.float32, device=dev)
+    bc = torch.empty((B, N), dtype=torch.int32, device=dev)
+    bt = torch.empty((B, N), dtype=torch.int32, device=dev)
+    need = lib().msa_route_aux_loss_workspace(ctypes.byref(d), B, M, C, N)
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, dev)
+    _check(lib().msa_route_aux_loss(ctypes.byref(d), _p(QR), B, M, _p(KRbar), _p(doc_chunk_offsets),
+                                    N, C, _p(pos), _p(n_pos), max_pos, float(tau), _p(loss),
+                                    _p(dQR), _p(dKR), _p(ds), _p(bc), _p(bt), _p(ws), ws.numel(),
+                                    _stream()))
+    return loss, dQR, dKR, ds, bc, bt
