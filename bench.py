@@ -53,12 +53,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", choices=["100m", "route16m", "pool10m", "interleave", "store",
-                                           "aux", "copy"],
+                                           "aux", "pipeline", "copy"],
                     default="100m")
     ap.add_argument("--layers", type=int, default=18)
     ap.add_argument("--chunks", type=int, default=1_562_500)
     ap.add_argument("--kv", choices=["host", "device"], default="host")
     ap.add_argument("--cpu-sample-chunks", type=int, default=400_000)
+    ap.add_argument("--queries", type=int, default=2, help="concurrent queries (pipeline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
@@ -686,6 +687,102 @@ def workload_aux(args):
     return r
 
 
+# ---------------------------------------------------------------------------
+# pipeline: concurrent decode queries over the 100M-token memory, one stream
+# per query, so one query's PCIe-bound attention overlaps another's scan
+# ---------------------------------------------------------------------------
+def workload_pipeline(args):
+    import numpy as np
+    import torch
+
+    import routed_sparse_attention_amd as msa
+    import synth
+
+    dev = "cuda"
+    L, Qn = args.layers, args.queries
+    store, queries, atts = synth.cfg4_100m(dev, n_chunks=args.chunks, n_layers=L,
+                                           kv_pinned=(args.kv == "host"))
+    torch.cuda.synchronize()
+    C, N = store.n_chunks, store.n_docs
+    d = msa.dims()
+    dco = torch.from_numpy(store.doc_chunk_offsets).to(dev)
+    max_sel = d.top_k * int(np.diff(store.doc_chunk_offsets).max())
+
+    class Lane:   # one query's buffers and stream (each query reuses the layer inputs)
+        def __init__(self):
+            self.stream = torch.cuda.Stream()
+            self.S = torch.empty((1, C), dtype=torch.float32, device=dev)
+            self.ds = torch.empty((1, N), dtype=torch.float32, device=dev)
+            self.outs = (torch.empty((1, d.top_k), dtype=torch.int32, device=dev),
+                         torch.empty((1, d.top_k), dtype=torch.float32, device=dev),
+                         torch.empty((1,), dtype=torch.int32, device=dev))
+            self.ws_sel = torch.empty(max(1, msa.lib().msa_select_topk_workspace(
+                ctypes.byref(d), 1, N)), dtype=torch.uint8, device=dev)
+            self.ws_att = torch.empty(msa.sparse_attend_workspace(
+                1, atts[0].K_loc.shape[0], max_sel, d), dtype=torch.uint8, device=dev)
+            self.out = torch.empty((1, 32, 128), dtype=torch.bfloat16, device=dev)
+
+        def layer(self, l):
+            msa.route_scores(queries[l].QR, store.KRbar[l], d, out=self.S)
+            msa.select_topk(self.S, dco, d, doc_scores=self.ds, ws=self.ws_sel, outs=self.outs)
+            msa.sparse_attend(atts[l].Q, atts[l].K_loc, atts[l].V_loc, store.Kbar, store.Vbar, dco,
+                              self.outs[0][0], self.outs[2], max_sel, d=d, ws=self.ws_att,
+                              out=self.out)
+
+    lanes = [Lane() for _ in range(Qn)]
+    torch.cuda.synchronize()
+
+    def run(concurrent):
+        """All queries through all layers; each query's layers in order on its
+        stream (concurrent) or every query on one stream, one after another."""
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        if concurrent:
+            for ln in lanes:
+                ln.stream.wait_event(ev0)
+            for l in range(L):
+                for ln in lanes:
+                    with torch.cuda.stream(ln.stream):
+                        ln.layer(l)
+            for ln in lanes:
+                torch.cuda.current_stream().wait_stream(ln.stream)
+        else:
+            for ln in lanes:
+                for l in range(L):
+                    ln.layer(l)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1)
+
+    for _ in range(args.warmup):
+        run(True)
+        run(False)
+    seq = [run(False) for _ in range(args.steps)]
+    conc = [run(True) for _ in range(args.steps)]
+    # every query still finds every layer's needle on its own stream
+    for ln in lanes:
+        for l in range(L):
+            with torch.cuda.stream(ln.stream):
+                ln.layer(l)
+            ln.stream.synchronize()
+            assert set(queries[l].planted_docs[0]) <= set(ln.outs[0][0].cpu().tolist())
+    ms_c, ms_s = float(np.mean(conc)), float(np.mean(seq))
+    tokens = C * TOKENS_PER_CHUNK
+    r = base_result(args, "memory tokens routed/sec (all concurrent queries)",
+                    Qn * L * tokens / (ms_c * 1e-3), "tokens/s", ms_c,
+                    {"workload": f"{Qn} concurrent decode queries, {L} routed layers each, over a "
+                                 f"{tokens / 1e6:.0f}M-token memory; K̄/V̄ "
+                                 f"{'in pinned host memory' if args.kv == 'host' else 'in HBM'}",
+                     "queries": Qn, "layers": L, "memory_tokens": tokens})
+    r.update({"ms_concurrent": ms_c, "ms_one_after_another": ms_s,
+              "speedup": ms_s / ms_c,
+              "per_query_latency_ms": ms_c,
+              "roofline": None, "cpu_baseline": None})
+    return r
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -697,7 +794,7 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     fn = {"100m": workload_100m, "route16m": workload_route16m, "pool10m": workload_pool10m,
-          "store": workload_store, "aux": workload_aux,
+          "store": workload_store, "aux": workload_aux, "pipeline": workload_pipeline,
           "interleave": workload_interleave, "copy": workload_copy}[args.workload]
     print(json.dumps(fn(args)), flush=True)
 
