@@ -228,7 +228,6 @@ int launch_parts_combine(const float* P, const RouteGeom& g, int64_t n_chunks,
                          int32_t token_reduce, float* S, hipStream_t s);
 
 // Doc reduce + top-k.
-constexpr int kTopkSlice = 1024;   // documents per stage-1 workgroup
 size_t doc_topk_workspace(int32_t B, int32_t n_docs, int32_t top_k);
 int launch_doc_topk(const float* S, int32_t B, int64_t n_chunks, const int64_t* dco,
                     int32_t n_docs, float* doc_scores, int32_t accumulate, int32_t top_k,

@@ -7,24 +7,28 @@
 // all are selected; a NaN score ranks below every number.
 //
 // Design.
-//   doc_max: a workgroup per (256 documents, query). The documents' chunk
+//   doc_max: a workgroup per (64 documents, query). The documents' chunk
 //     range is contiguous; it streams through a 32 KiB LDS tile with
-//     coalesced loads (all 32 loads of a thread in flight), then each thread
-//     max-reduces its own document's chunks from LDS (NaN propagates, as
-//     numpy's max does), max-merges with the previous score when
-//     accumulating, and writes the document score.
+//     coalesced loads (all 32 loads of a thread in flight), then four threads
+//     per document max-reduce its chunks from LDS and combine by DPP (NaN
+//     propagates, as numpy's max does), max-merge with the previous score
+//     when accumulating, and write the document score and the best key of
+//     the 64 documents.
 //   topk_select: one 1024-thread workgroup per query. Each document becomes
 //     the unique 64-bit key (order-preserving uint32 of the score) << 32 |
 //     (0xFFFFFFFF − id), so larger key = better document and equal scores
 //     fall back to the lower id (NaN maps to the lowest scores).
-//     Fast path: doc_max also writes the best key of every block of 256
-//     documents. T = the k-th best block maximum is reached by at least k
-//     documents, and only blocks whose maximum reaches T (about k of them)
-//     can hold a key >= T; those keys are ballot-compacted into LDS and
-//     sorted, and the head of the list is the answer. Keys are distinct (the
-//     id is part of the key), so lists of up to 256 keys are sorted in one
-//     step by rank counting (each key's rank = number of larger keys);
-//     longer ones by a bitonic network.
+//     Up to 2048 documents: all keys are sorted. Beyond: the best key of
+//     every block of bs documents (bs the largest power of two <= 256 that
+//     leaves at least k blocks; combined from doc_max's 64-document maxima),
+//     and T = the k-th best block
+//     maximum is reached by at least k documents; only blocks whose maximum
+//     reaches T — exactly k of them, block maxima being distinct — can hold
+//     a key >= T; those keys are ballot-compacted into LDS and sorted, and
+//     the head of the list is the answer. Keys are distinct (the id is part
+//     of the key), so lists of up to 256 keys are sorted in one step by rank
+//     counting (each key's rank = number of larger keys); longer ones by a
+//     bitonic network.
 //     Fallback (massive ties at T, or more than 2048 blocks):
 //     radix select on the uint32 score keys. Four passes
 //     over 8-bit digits, most significant first, histogram the keys that
@@ -58,12 +62,14 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// The 256 documents of a block own one contiguous chunk range (the chunk
+// The 64 documents of a block own one contiguous chunk range (the chunk
 // plan keeps documents contiguous). The block streams that range through an
-// LDS tile with coalesced loads; each thread then takes the max over its own
-// document's chunks in the tile.
+// LDS tile with coalesced loads (all of a thread's loads in flight); four
+// threads then share each document, striding over its chunks in the tile,
+// and combine with two DPP steps.
+constexpr int kDocsPerBlock = 64;
 constexpr int kDocTile = 8192;   // chunk scores per LDS tile (32 KiB)
-constexpr int kDocLoads = kDocTile / kMaxThreads;   // 32 loads per thread, all in flight
+constexpr int kDocLoads = kDocTile / kMaxThreads;   // 32 loads per thread
 
 __global__ __launch_bounds__(256) void doc_max_kernel(const float* __restrict__ S, int64_t C,
                                                       const int64_t* __restrict__ dco,
@@ -74,9 +80,10 @@ __global__ __launch_bounds__(256) void doc_max_kernel(const float* __restrict__ 
   __shared__ float tile[kDocTile];
   __shared__ uint64_t wbest[kMaxThreads / 64];
   const int b = blockIdx.y;
-  const int64_t d0 = (int64_t)blockIdx.x * kMaxThreads;
-  const int64_t d1 = min(d0 + kMaxThreads, (int64_t)n_docs);
-  const int64_t i = d0 + threadIdx.x;
+  const int64_t d0 = (int64_t)blockIdx.x * kDocsPerBlock;
+  const int64_t d1 = min(d0 + kDocsPerBlock, (int64_t)n_docs);
+  const int sub = threadIdx.x & 3;
+  const int64_t i = d0 + (threadIdx.x >> 2);
   auto clampc = [&](int64_t c) { return max((int64_t)0, min(c, C)); };
   const int64_t r0 = clampc(dco[d0]), r1 = max(r0, clampc(dco[d1]));
   int64_t c0 = 0, c1 = 0;
@@ -97,20 +104,22 @@ __global__ __launch_bounds__(256) void doc_max_kernel(const float* __restrict__ 
     for (int u = 0; u < kDocLoads; ++u) tile[threadIdx.x + u * kMaxThreads] = v[u];
     __syncthreads();
     const int a = (int)(max(c0, t0) - t0), e = (int)(min(c1, t0 + n) - t0);
-#pragma unroll 8
-    for (int c = a; c < e; ++c) s = nan_max(s, tile[c]);
+#pragma unroll 4
+    for (int c = a + sub; c < e; c += 4) s = nan_max(s, tile[c]);
     __syncthreads();
   }
+  s = nan_max(s, dpp_f<0xB1>(s));   // the document's four threads (a lane quad)
+  s = nan_max(s, dpp_f<0x4E>(s));
   uint64_t key = 0;
-  if (i < n_docs) {
+  if (i < n_docs && sub == 0) {
     float* ds = doc_scores + (int64_t)b * n_docs + i;
     if (accumulate) s = nan_max(*ds, s);
     *ds = s;
     key = doc_key(s, i);
   }
-  // the best document key of this block of 256 documents
+  // the best key of these 64 documents, for the top-k threshold
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
+  for (int o = 4; o < 64; o <<= 1) {
     const uint64_t y = shfl_xor_u64(key, o);
     key = y > key ? y : key;
   }
@@ -255,9 +264,8 @@ __device__ void sort_cand_desc(uint64_t* cand, int n) {
 }
 
 __global__ __launch_bounds__(1024) void topk_select_kernel(const float* __restrict__ doc_scores,
-                                                           const uint64_t* __restrict__ bmax,
-                                                           int32_t n_blocks, int32_t N,
-                                                           int32_t K,
+                                                           const uint64_t* __restrict__ bmax64,
+                                                           int32_t bs, int32_t N, int32_t K,
                                                            int32_t* __restrict__ topk_ids,
                                                            float* __restrict__ topk_scores,
                                                            int32_t* __restrict__ n_sel) {
@@ -272,33 +280,64 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(const float* __restri
   const int tid = threadIdx.x, lane = tid & 63;
   const int b = blockIdx.x;
   const float* s = doc_scores + (int64_t)b * N;
-  const uint64_t* bm = bmax + (int64_t)b * n_blocks;
   const int Ks = N < K ? N : K;
+  const int n_blocks = (N + bs - 1) / bs;
+  const int wave = tid >> 6;
 
   int cnt = kCandCap + 1;  // forces the fallback unless the fast path applies
-  if (n_blocks >= K && n_blocks <= kCandCap) {
+  if (N > kCandCap && n_blocks >= K && n_blocks <= kCandCap) {
     // ---- T = K-th best block maximum: at least K documents reach it, and a
     //      document at or above T can only sit in a block whose maximum does
-    for (int i = tid; i < n_blocks; i += kSelThreads) cand[i] = bm[i];
+    // block maxima over blocks of bs documents: from doc_max's maxima of 64
+    // documents when bs is a multiple of 64, else one wave per block
+    const int nb64 = (N + kDocsPerBlock - 1) / kDocsPerBlock;
+    const uint64_t* bm = bmax64 + (int64_t)b * nb64;
+    const int r = bs / kDocsPerBlock;
+    if (r >= 1) {
+      for (int j = tid; j < n_blocks; j += kSelThreads) {
+        uint64_t key = 0;
+        for (int q = 0; q < r; ++q) {
+          const int x = j * r + q;
+          const uint64_t y = x < nb64 ? bm[x] : 0ull;
+          key = y > key ? y : key;
+        }
+        cand[j] = key;
+      }
+    } else for (int j = wave; j < n_blocks; j += kSelWaves) {
+      uint64_t key = 0;
+      for (int i = lane; i < bs; i += 64) {
+        const int d = j * bs + i;
+        if (d < N) {
+          const uint64_t k2 = doc_key(s[d], d);
+          key = k2 > key ? k2 : key;
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t y = shfl_xor_u64(key, o);
+        key = y > key ? y : key;
+      }
+      if (lane == 0) cand[j] = key;
+    }
     if (tid == 0) n_cand = 0;
     __syncthreads();
     sort_cand_desc(cand, n_blocks);
     const uint64_t T = cand[K - 1];
     // block maxima are distinct, so exactly the first K blocks reach T
     const int n_hot = K;
-    if (tid < n_hot) hot[tid] = (int)((0xFFFFFFFFu - (uint32_t)(cand[tid] & 0xFFFFFFFFu)) / kMaxThreads);
+    if (tid < n_hot) hot[tid] = (int)((0xFFFFFFFFu - (uint32_t)(cand[tid] & 0xFFFFFFFFu)) / bs);
     __syncthreads();
-    // ---- gather keys >= T from the hot blocks (256 documents each); every
+    // ---- gather keys >= T from the hot blocks (bs documents each); every
     //      load of a thread is issued before the compaction
-    constexpr int kPer = kMaxK * kMaxThreads / kSelThreads;
-    const int total = n_hot * kMaxThreads;
+    constexpr int kPer = kMaxK * kMaxThreads / kSelThreads;   // bs <= kMaxThreads
+    const int total = n_hot * bs;
     uint64_t kk[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int j = u * kSelThreads + tid;
       kk[u] = 0;
       if (j < total) {
-        const int64_t i = (int64_t)hot[j / kMaxThreads] * kMaxThreads + (j % kMaxThreads);
+        const int64_t i = (int64_t)hot[j / bs] * bs + (j % bs);
         if (i < N) kk[u] = doc_key(s[i], i);
       }
     }
@@ -360,8 +399,8 @@ __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
 
 size_t doc_topk_workspace(int32_t B, int32_t n_docs, int32_t top_k) {
   (void)top_k;
-  const int64_t n_blocks = (n_docs + kMaxThreads - 1) / kMaxThreads;
-  return align_up((size_t)B * n_blocks * sizeof(uint64_t), 256);
+  const int64_t nb64 = (n_docs + kDocsPerBlock - 1) / kDocsPerBlock;
+  return align_up((size_t)B * nb64 * sizeof(uint64_t), 256);
 }
 
 int launch_doc_topk(const float* S, int32_t B, int64_t n_chunks, const int64_t* dco,
@@ -369,12 +408,16 @@ int launch_doc_topk(const float* S, int32_t B, int64_t n_chunks, const int64_t* 
                     uint64_t* cand, int32_t* topk_ids, float* topk_scores, int32_t* n_sel,
                     hipStream_t s) {
   if (top_k > kMaxK) return fail(MSA_ERR_UNSUPPORTED, "top_k > %d", kMaxK);
-  const unsigned blocks = (unsigned)((n_docs + kMaxThreads - 1) / kMaxThreads);
+  const unsigned blocks = (unsigned)((n_docs + kDocsPerBlock - 1) / kDocsPerBlock);
   hipLaunchKernelGGL(doc_max_kernel, dim3(blocks, B), dim3(kMaxThreads), 0, s, S, n_chunks, dco,
                      n_docs, doc_scores, accumulate, cand);
   MSA_LAUNCH_CHECK("doc_max_kernel launch");
-  hipLaunchKernelGGL(topk_select_kernel, dim3(B), dim3(kSelThreads), 0, s, doc_scores, cand,
-                     (int32_t)blocks, n_docs, top_k, topk_ids, topk_scores, n_sel);
+  // threshold blocks: the largest power of two <= 256 documents that still
+  // gives at least top_k blocks
+  int bs = kMaxThreads;
+  while (bs > 1 && (n_docs + bs - 1) / bs < top_k) bs >>= 1;
+  hipLaunchKernelGGL(topk_select_kernel, dim3(B), dim3(kSelThreads), 0, s, doc_scores, cand, bs,
+                     n_docs, top_k, topk_ids, topk_scores, n_sel);
   MSA_LAUNCH_CHECK("topk_select_kernel launch");
   return MSA_OK;
 }
