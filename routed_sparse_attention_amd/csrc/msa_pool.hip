@@ -24,8 +24,9 @@
 //     host supplies cos ω_m, sin ω_m in fp64, and a chunk that does not
 //     continue the previous one (a wave's first chunk, CHUNK mode) reaches its
 //     angle by square-and-multiply of that one-step rotation;
-//   - token loads are branch-free (clamped indices, masked values), so a
-//     group of tokens' loads (8 plain, 4 with RoPE) is in flight at once.
+//   - token loads are branch-free (clamped indices, masked values) and go
+//     into two register sets taken in turn (4 tokens per group plain, 2 with
+//     RoPE): one group is summed while the next is in flight.
 #include <cmath>
 
 #include "msa_internal.h"
@@ -139,18 +140,20 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a, int32_t first_ten
     for (int e = 0; e < 16; ++e) acc[e] = 0.0;
 
     // Branch-free loads: token indices past the chunk's end are clamped to
-    // its last token (always in bounds) and their values masked out, so all
-    // kUnroll pairs of loads of a group are in flight together.
+    // its last token (always in bounds) and their values masked out. Two
+    // register sets take turns: a group of kUnroll tokens is summed while the
+    // next group's loads are in flight.
     const uint4* row = src4 + t0 * kRowVec;
     const int last = n > 0 ? n - 1 : 0;
-    for (int t = 0; t < n; t += kUnroll) {
-      uint4 x0[kUnroll], x1[kUnroll];
+    auto load = [&](int t, uint4* x0, uint4* x1) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int64_t tt = min(t + u, last);
         x0[u] = load_stream(row + tt * kRowVec + idx0);
         x1[u] = load_stream(row + tt * kRowVec + idx1);
       }
+    };
+    auto consume = [&](int t, const uint4* x0, const uint4* x1) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         // a clamped duplicate contributes +0 (its words are zeroed)
@@ -177,6 +180,18 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a, int32_t first_ten
           }
         }
       }
+    };
+    uint4 xa[kUnroll], xb[kUnroll], ya[kUnroll], yb[kUnroll];
+    load(0, xa, xb);
+    for (int t = 0;;) {
+      load(t + kUnroll, ya, yb);
+      consume(t, xa, xb);
+      t += kUnroll;
+      if (t >= n) break;
+      load(t + kUnroll, xa, xb);
+      consume(t, ya, yb);
+      t += kUnroll;
+      if (t >= n) break;
     }
     if (tok_rope) {
       // the recurrence advanced past the chunk's end by the masked tail steps;
@@ -216,7 +231,7 @@ int launch_pool(const PoolArgs& args, hipStream_t s) {
   // V and K^R (plain means), then K (document RoPE): separate instantiations
   // so the plain pass does not carry the rotation state's registers
   if (a.Vbar || a.KRbar) {
-    hipLaunchKernelGGL((pool_kernel<false, 8>), dim3(n_wg, 2), dim3(256), 0, s, a, 1);
+    hipLaunchKernelGGL((pool_kernel<false, 4>), dim3(n_wg, 2), dim3(256), 0, s, a, 1);
     MSA_LAUNCH_CHECK("pool_kernel<plain> launch");
   }
   if (a.Kbar) {
