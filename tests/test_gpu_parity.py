@@ -380,3 +380,54 @@ def test_select_topk_fallback_paths(case):
         assert list(ids[b].cpu().numpy()[:n]) == list(exp_ids)
         assert np.array_equal(sc[b].cpu().numpy()[:n].astype(np.float64), exp_sc)
         assert all(x == -1 for x in ids[b].cpu().numpy()[n:])
+
+
+@pytest.mark.parametrize("n_chunks", [1, 2, 5, 31, 33, 3001])
+@pytest.mark.parametrize("B,M", [(1, 1), (9, 1), (2, 13)])
+def test_route_ragged_chunk_counts(n_chunks, B, M):
+    """Chunk counts that fill no tile, end mid-tile, or are not a multiple of
+    four, on both scans (8 rows or fewer: VALU; more: MFMA)."""
+    _banner(f"route n_chunks={n_chunks} B={B} M={M}")
+    st = _store(n_chunks, 500 + n_chunks, lo=1, hi=7)
+    QR = synth.randn_bf16((B, M, 8, 128), synth.torch_gen(9, n_chunks * 100 + B * 10 + M))
+    _check_route(QR, st, msa.dims())
+
+
+def _doc_scores_case(rng, case):
+    """fp32 chunk scores for the threshold paths of the top-k select."""
+    n_docs, k = {"bs128_nan": (3000, 16), "bs256_ragged": (20_000, 16), "wave_bs32": (2100, 40),
+                 "k64_wave": (2500, 64), "k64_bs256": (70_000, 64), "tie_top": (20_000, 16),
+                 "blocks_over_2048": (600_000, 16)}[case]
+    counts = rng.integers(1, 4, size=n_docs)
+    dco_h = synth.offsets_from_lengths(counts)
+    C = int(dco_h[-1])
+    S = rng.standard_normal((2, C)).astype(np.float32)
+    if case == "bs128_nan":
+        S[:, rng.choice(C, size=50, replace=False)] = np.nan
+    if case == "tie_top":
+        # 40 documents spread over many blocks share the best score exactly
+        for b in range(2):
+            docs = rng.choice(n_docs, size=40, replace=False)
+            S[b, dco_h[docs]] = 9.0
+    return S, dco_h, k
+
+
+@pytest.mark.parametrize("case", ["bs128_nan", "bs256_ragged", "wave_bs32", "k64_wave", "k64_bs256",
+                                  "tie_top", "blocks_over_2048"])
+def test_select_topk_threshold_paths(case):
+    """Above 2048 documents the select thresholds on block maxima; the block
+    size depends on N and k (down to one wave per 32-document block), and past
+    2048 blocks it takes the radix path. Every form is exact."""
+    _banner(f"select_topk threshold path {case}")
+    rng = synth.np_rng(94, len(case))
+    S, dco_h, k = _doc_scores_case(rng, case)
+    d = msa.dims(top_k=k)
+    ds, ids, sc, ns = msa.select_topk(torch.from_numpy(S).to(DEV), torch.from_numpy(dco_h).to(DEV), d)
+    torch.cuda.synchronize()
+    for b in range(S.shape[0]):
+        s = O.doc_scores(S[b].astype(np.float64), dco_h)
+        assert np.array_equal(ds[b].cpu().numpy().astype(np.float64), s, equal_nan=True)
+        exp_ids, exp_sc, _ = O.topk(s, k)
+        assert int(ns[b]) == k
+        assert list(ids[b].cpu().numpy()) == list(exp_ids)
+        assert np.array_equal(sc[b].cpu().numpy().astype(np.float64), exp_sc)
