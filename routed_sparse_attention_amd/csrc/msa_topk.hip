@@ -8,12 +8,13 @@
 //
 // Design.
 //   doc_max: a workgroup per (64 documents, query). The documents' chunk
-//     range is contiguous; it streams through a 32 KiB LDS tile with
-//     coalesced loads (all 32 loads of a thread in flight), then four threads
+//     range is contiguous; it streams through a 16 KiB LDS tile with
+//     coalesced loads (all 16 loads of a thread in flight), then four threads
 //     per document max-reduce its chunks from LDS and combine by DPP (NaN
 //     propagates, as numpy's max does), max-merge with the previous score
 //     when accumulating, and write the document score and the best key of
-//     the 64 documents.
+//     the 64 documents. (Looping a workgroup over several queries, with the
+//     next query's loads in flight, measured slower: fewer workgroups.)
 //   topk_select: one 1024-thread workgroup per query. Each document becomes
 //     the unique 64-bit key (order-preserving uint32 of the score) << 32 |
 //     (0xFFFFFFFF − id), so larger key = better document and equal scores
@@ -68,8 +69,8 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
 // threads then share each document, striding over its chunks in the tile,
 // and combine with two DPP steps.
 constexpr int kDocsPerBlock = 64;
-constexpr int kDocTile = 8192;   // chunk scores per LDS tile (32 KiB)
-constexpr int kDocLoads = kDocTile / kMaxThreads;   // 32 loads per thread
+constexpr int kDocTile = 4096;   // chunk scores per LDS tile (16 KiB: 8 blocks per CU)
+constexpr int kDocLoads = kDocTile / kMaxThreads;   // 16 loads per thread
 
 __global__ __launch_bounds__(256) void doc_max_kernel(const float* __restrict__ S, int64_t C,
                                                       const int64_t* __restrict__ dco,
@@ -95,13 +96,19 @@ __global__ __launch_bounds__(256) void doc_max_kernel(const float* __restrict__ 
   float s = -INFINITY;
   for (int64_t t0 = r0; t0 < r1; t0 += kDocTile) {
     const int n = (int)min((int64_t)kDocTile, r1 - t0);
-    // every load is issued before any store waits on one (indices past the
-    // range are clamped into it and never read back)
+    // every load is issued before any store waits on one; slots past the
+    // range are neither loaded nor read back
     float v[kDocLoads];
 #pragma unroll
-    for (int u = 0; u < kDocLoads; ++u) v[u] = Sb[t0 + min((int)threadIdx.x + u * kMaxThreads, n - 1)];
+    for (int u = 0; u < kDocLoads; ++u) {
+      const int c = (int)threadIdx.x + u * kMaxThreads;
+      if (c < n) v[u] = Sb[t0 + c];
+    }
 #pragma unroll
-    for (int u = 0; u < kDocLoads; ++u) tile[threadIdx.x + u * kMaxThreads] = v[u];
+    for (int u = 0; u < kDocLoads; ++u) {
+      const int c = (int)threadIdx.x + u * kMaxThreads;
+      if (c < n) tile[c] = v[u];
+    }
     __syncthreads();
     const int a = (int)(max(c0, t0) - t0), e = (int)(min(c1, t0 + n) - t0);
 #pragma unroll 4
@@ -233,17 +240,23 @@ __device__ void bitonic_desc(uint64_t* a, int n2) {
   }
 }
 
-// Sorts n <= kSelThreads distinct keys of a[] descending into out[] (a and
-// out must not overlap): a key's rank is the number of larger keys.
-constexpr int kRankMax = 256;
+// Sorts n <= kRankMax distinct keys of a[] descending into out[] (a and out
+// must not overlap): a key's rank is the number of larger keys. The four
+// threads of a lane quad share a key, each counting every fourth key, so the
+// serial LDS loop is n / 4 long.
+constexpr int kRankMax = kSelThreads / 4;
 __device__ void rank_sort_desc(const uint64_t* a, uint64_t* out, int n) {
-  const int tid = threadIdx.x;
-  if (tid < n) {
-    const uint64_t x = a[tid];
-    int r = 0;
-    for (int j = 0; j < n; ++j) r += a[j] > x ? 1 : 0;
-    out[r] = x;
+  const int i = threadIdx.x >> 2, q = threadIdx.x & 3;
+  uint64_t x = 0;
+  int r = 0;
+  if (i < n) {
+    x = a[i];
+#pragma unroll 8
+    for (int j = q; j < n; j += 4) r += a[j] > x ? 1 : 0;
   }
+  r += __shfl_xor(r, 1);
+  r += __shfl_xor(r, 2);
+  if (i < n && q == 0) out[r] = x;
   __syncthreads();
 }
 
@@ -296,9 +309,10 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(const float* __restri
     if (r >= 1) {
       for (int j = tid; j < n_blocks; j += kSelThreads) {
         uint64_t key = 0;
-        for (int q = 0; q < r; ++q) {
+#pragma unroll
+        for (int q = 0; q < kMaxThreads / kDocsPerBlock; ++q) {
           const int x = j * r + q;
-          const uint64_t y = x < nb64 ? bm[x] : 0ull;
+          const uint64_t y = (q < r && x < nb64) ? bm[x] : 0ull;
           key = y > key ? y : key;
         }
         cand[j] = key;
