@@ -34,7 +34,7 @@
 namespace msa {
 namespace {
 
-constexpr int kChunksPerWave = 4;
+constexpr int kChunksPerWave = 2;   // (1, 2, 4, 8, 16 measured: 2 is fastest)
 constexpr int kWavesPerWG = 4;
 
 // Largest i in [0, n_docs-1] with dco[i] <= c (document holding chunk c).
