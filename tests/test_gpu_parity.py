@@ -202,15 +202,19 @@ def test_route_deterministic():
 # ---------------------------------------------------------------------------
 # sparse attention (stage 3)
 # ---------------------------------------------------------------------------
-def _attend_case(M, M_loc, counts, sel, seed, host_kv=False, pos0=-1, k_rot=False, top_k=16):
+def _attend_case(M, M_loc, counts, sel, seed, host_kv=False, pos0=-1, k_rot=False, top_k=16,
+                 sel_gpu=None):
+    """sel: the selection the oracle attends over; sel_gpu (default sel): the
+    ids the GPU is given, which may hold invalid ids that it must skip."""
     st = synth.pooled_store(counts, seed, "cpu", with_kv=True)
     att = synth.attend_inputs(M, M_loc, seed)
     dco_h = st.doc_chunk_offsets
     d = msa.dims(top_k=top_k)
+    sel_gpu = sel if sel_gpu is None else sel_gpu
     sel_pad = np.full(top_k, -1, np.int32)
-    sel_pad[:len(sel)] = sel
+    sel_pad[:len(sel_gpu)] = sel_gpu
     sel_t = torch.from_numpy(sel_pad).to(DEV)
-    ns_t = torch.tensor([len(sel)], dtype=torch.int32, device=DEV)
+    ns_t = torch.tensor([len(sel_gpu)], dtype=torch.int32, device=DEV)
     if host_kv:
         Kb = st.Kbar.pin_memory()
         Vb = st.Vbar.pin_memory()
@@ -264,6 +268,33 @@ def test_attend_long_local():
     _banner("attend M=256 M_loc=700")
     counts = [64] * 10 + [100, 128, 7]
     _attend_case(256, 700, counts, [10, 11, 0, 5, 12, 3], 76)
+
+
+@pytest.mark.parametrize("M,M_loc,pos0", [(1, 40, 70_000), (3, 35, 1_000_003), (8, 71, 12_345),
+                                           (9, 40, 123_456), (1, 33, -1)])
+def test_attend_rope_positions(M, M_loc, pos0):
+    """Global RoPE of Q and local K at large positions: up to 8 query tokens
+    rotate their local keys inside the attention waves, 9 use the separate
+    rotation kernel; local tiles straddle the memory/local boundary."""
+    _banner(f"attend RoPE M={M} M_loc={M_loc} pos0={pos0}")
+    counts = [5, 17, 2, 64, 9, 33, 1, 12, 40, 7, 3, 21]
+    sel = [3, 8, 0, 11, 5, 1, 9, 6, 2, 10]
+    _attend_case(M, M_loc, counts, sel, 78 + M, pos0=pos0)
+
+
+def test_attend_k64_with_invalid_ids():
+    """top_k = 64 (the chunk list's largest search), with invalid ids mixed
+    into the selection: the GPU skips them, so it must equal the oracle over
+    the valid ids in the same order (pos0 given, since n_sel counts them)."""
+    _banner("attend top_k=64, invalid ids skipped")
+    rng = synth.np_rng(79, 0)
+    counts = rng.integers(1, 4, size=80)
+    valid = [int(x) for x in rng.choice(80, size=60, replace=False)]
+    sel_gpu = list(valid)
+    for pos, bad in ((0, -1), (17, 80), (33, 10 ** 6), (63, -7)):
+        sel_gpu.insert(pos, bad)
+    assert len(sel_gpu) == 64
+    _attend_case(2, 50, counts, valid, 79, pos0=64, top_k=64, sel_gpu=sel_gpu)
 
 
 def test_attend_rejects_pageable_host_kv():
