@@ -12,12 +12,13 @@
 // Design: a workgroup of 8 waves holds 64 query rows; each wave owns whole
 // 32-chunk tiles (all 8 heads) and strides over the store on its own, with no
 // barrier once the rows are staged:
-//   - q̂ = Q^R / max(‖Q^R‖, eps) (fp64 norm), rounded once to bf16 (the
-//     rounding moves a cosine by ~1e-4, inside the 1e-3 score tolerance; the
-//     decode scan keeps a hi + lo split instead), is laid out in LDS as MFMA A
-//     fragments [head][row block][k-step][lane] (128 KiB), so every fragment
-//     read is one contiguous ds_read_b128 per lane; each fragment read serves
-//     the tile's two 16-chunk column blocks;
+//   - q̂ = Q^R / max(‖Q^R‖, eps) (fp64 norm; the scaled value is formed in
+//     fp32 and rounded to bf16, which moves a cosine by ~1e-4, inside the 1e-3
+//     score tolerance; the decode scan keeps a hi + lo split instead) is
+//     prepared while the wave's first key loads are in flight and laid out in
+//     LDS as MFMA A fragments [head][row block][k-step][lane] (128 KiB), so
+//     every fragment read is one contiguous ds_read_b128 per lane; each
+//     fragment read serves the tile's two 16-chunk column blocks;
 //   - keys: the B operand puts four lanes on each chunk column, so every load
 //     instruction reads 64 contiguous bytes of each of 16 chunk rows (the
 //     L1→L2 request size of a fully coalesced load). Two heads' loads are in
@@ -83,6 +84,28 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(const uint16_t* __r
   const int grp = lane >> 4;
   const int nr_u = g.M < kSegRows ? g.M : kSegRows;   // rows per segment
 
+  const int64_t n_ct = (n_chunks + kChunkTile - 1) / kChunkTile;
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  int64_t t = (int64_t)blockIdx.x * kWaves + wave;
+
+  // Columns past the end (and tiles past the last) reload the last chunk, so
+  // the loads stay unconditional and the compiler waits on exactly the head it
+  // is about to use. Those scores are not stored.
+  auto load_head = [&](int64_t tile, int h, uint4 (&buf)[kCB][kKSteps]) {
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      int64_t c = tile * kChunkTile + cb * 16 + col;
+      c = c < n_chunks ? c : n_chunks - 1;
+      const uint4* src = KR + (c * kHeads + h) * (kDim / 8) + grp;
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) buf[cb][ks] = src[4 * ks];
+    }
+  };
+
+  // A ring of kRing head buffers over the (tile, head) sequence: a buffer is
+  // refilled with the step kRing ahead as soon as its head has been used.
+  uint4 kb[kRing][kCB][kKSteps];
+
   // ---- stage q̂: thread = (A row tid / 8, head tid % 8), 128 dims each
   {
     const int r = tid >> 3, h = tid & 7;
@@ -104,10 +127,21 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(const uint16_t* __r
       }
       row = (int64_t)(tr.b0 + s) * g.M + tr.m0 + m;
     }
+    if (!ok) row = 0;   // loaded (always in bounds) and zeroed below
     uint4 raw[16];
     const uint4* src = reinterpret_cast<const uint4*>(QR + (row * kHeads + h) * kDim);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) raw[i] = ok ? src[i] : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 16; ++i) raw[i] = src[i];
+    // this wave's first key loads fly while q̂ is prepared (the scheduling
+    // barriers keep the row loads ahead of them, so waiting for the rows does
+    // not wait for the keys)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) load_head(t, k, kb[k]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (!ok) raw[i] = make_uint4(0, 0, 0, 0);
     // squares of bf16 values are exact in fp32; the sum runs in fp64
     double ss = 0.0;
 #pragma unroll
@@ -120,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(const uint16_t* __r
       }
     }
     const double nrm = sqrt(ss);
-    const double inv = 1.0 / (nrm > (double)kNormEps ? nrm : (double)kNormEps);
+    const float inv = (float)(1.0 / (nrm > (double)kNormEps ? nrm : (double)kNormEps));
     const int rb = r >> 4;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -129,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(const uint16_t* __r
       uint32_t hw[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        hw[j] = pack2(d2bf((double)bf16lo(w[j]) * inv), d2bf((double)bf16hi(w[j]) * inv));
+        hw[j] = pack2(f2bf(bf16lo(w[j]) * inv), f2bf(bf16hi(w[j]) * inv));
       const int frag = (h * 4 + rb) * kKSteps + (i >> 2);
       qs[frag * 64 + (r & 15) + 16 * (i & 3)] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     }
@@ -144,24 +178,7 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(const uint16_t* __r
   const float fin = (mean && g.parts == 1) ? 0.125f / (float)g.M : 0.125f;   // with the head mean
   const float eps2 = kNormEps * kNormEps;
 
-  const int64_t n_ct = (n_chunks + kChunkTile - 1) / kChunkTile;
-  const int64_t stride = (int64_t)gridDim.x * kWaves;
-  int64_t t = (int64_t)blockIdx.x * kWaves + wave;
   if (t >= n_ct) return;
-
-  // Columns past the end (and tiles past the last) reload the last chunk, so
-  // the loads stay unconditional and the compiler waits on exactly the head it
-  // is about to use. Those scores are not stored.
-  auto load_head = [&](int64_t tile, int h, uint4 (&buf)[kCB][kKSteps]) {
-#pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-      int64_t c = tile * kChunkTile + cb * 16 + col;
-      c = c < n_chunks ? c : n_chunks - 1;
-      const uint4* src = KR + (c * kHeads + h) * (kDim / 8) + grp;
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) buf[cb][ks] = src[4 * ks];
-    }
-  };
 
   f32x4_t tot[kCB][4];
   auto head = [&](int h, const uint4 (&kb)[kCB][kKSteps]) {
@@ -270,11 +287,6 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(const uint16_t* __r
     }
   };
 
-  // A ring of kRing head buffers over the (tile, head) sequence: a buffer is
-  // refilled with the step kRing ahead as soon as its head has been used.
-  uint4 kb[kRing][kCB][kKSteps];
-#pragma unroll
-  for (int h = 0; h < kRing; ++h) load_head(t, h, kb[h]);
   while (true) {
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb)
