@@ -367,6 +367,7 @@ int32_t msa_sparse_attend(const msa_dims* d, const msa_bf16* Q, int32_t M, const
   a.n_chunks = n_chunks; a.dco = dco; a.n_docs = n_docs;
   a.sel_ids = sel_ids; a.n_sel = n_sel; a.top_k = d->top_k;
   a.max_sel_chunks = max_sel_chunks; a.pos0 = pos0; a.theta = (double)d->rope_theta;
+  a.kv_on_host = kv_on_host ? 1 : 0;
   a.out = out; a.out_f32 = out_f32;
   return launch_attend(a, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
@@ -441,6 +442,7 @@ int32_t msa_interleave_step(const msa_dims* d, msa_interleave_state* st, const m
   a.n_chunks = n_chunks; a.dco = dco; a.n_docs = n_docs;
   a.sel_ids = st->topk_ids; a.n_sel = st->n_sel; a.top_k = d->top_k;
   a.max_sel_chunks = max_sel_chunks; a.pos0 = st->pos0; a.theta = (double)d->rope_theta;
+  a.kv_on_host = kv_on_host ? 1 : 0;
   a.out = out; a.out_f32 = nullptr;
   rc = launch_attend(a, ws, ws_bytes, s);
   if (rc) return rc;

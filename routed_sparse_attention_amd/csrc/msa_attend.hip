@@ -167,7 +167,14 @@ constexpr int kMaxSel = 64;   // top_k bound
 // (fields: vmcnt bits 3:0 and 15:14, expcnt bits 6:4, lgkmcnt bits 11:8)
 constexpr int kWaitVm2 = 2 | (7 << 4) | (15 << 8);
 
-__global__ __launch_bounds__(64) void attn_kernel(const AttnArgs a) {
+// HOST_KV: K̄/V̄ are read from pinned host memory over PCIe. Those reads are
+// throttled (below) and the kernel keeps its full register budget; with
+// device memory the loads are not throttled and the kernel is held to two
+// waves per SIMD (measured: a 128-token query over 2K selected chunks 85 ->
+// 60 us; decode unchanged).
+template <bool HOST_KV>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(HOST_KV ? 1 : 2)))
+void attn_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kKsBytes + kVtBytes + kPsBytes];
   __shared__ int32_t s_off[kMaxSel];
   __shared__ int64_t s_start[kMaxSel];
@@ -305,11 +312,12 @@ __global__ __launch_bounds__(64) void attn_kernel(const AttnArgs a) {
                               : ((int64_t)(j - n_mem) * kHeads + g) * kDim;
       kx[it] = reinterpret_cast<gu32x4*>((mem ? Kbar : Kloc) + off)[dv];
       vx[it] = reinterpret_cast<gu32x4*>((mem ? Vbar : Vloc) + off)[dv];
-      // at most two K/V pairs of a wave in flight: with all sixteen issued at
-      // once by every wave, reads of pinned host memory over PCIe measured
-      // slower (decode, 16 documents: 63.5 vs 58.0 us per call); device
-      // memory is indifferent (19.9 vs 20.0 us)
-      __builtin_amdgcn_s_waitcnt(kWaitVm2);
+      // host K̄/V̄: at most two K/V pairs of a wave in flight. With all
+      // sixteen issued at once by every wave, reads of pinned host memory
+      // over PCIe measured slower (decode, 16 documents: 63.5 vs 58.0 us per
+      // call); from device memory all sixteen go out at once (256 query
+      // tokens over 2K chunks: 146 -> 132 us per call)
+      if (HOST_KV) __builtin_amdgcn_s_waitcnt(kWaitVm2);
     }
 
     // ---- first tile: the A fragments of this lane's query row (row =
@@ -602,7 +610,10 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s)
     MSA_LAUNCH_CHECK("rot_k_kernel launch");
     k.Kloc = Kr;
   }
-  hipLaunchKernelGGL(attn_kernel, dim3(p.row_blocks, kHeads, p.n_splits), dim3(64), 0, s, k);
+  if (a.kv_on_host)
+    hipLaunchKernelGGL(attn_kernel<true>, dim3(p.row_blocks, kHeads, p.n_splits), dim3(64), 0, s, k);
+  else
+    hipLaunchKernelGGL(attn_kernel<false>, dim3(p.row_blocks, kHeads, p.n_splits), dim3(64), 0, s, k);
   MSA_LAUNCH_CHECK("attn_kernel launch");
 
   const int64_t n_rows = (int64_t)a.M * a.n_q_heads;

@@ -249,6 +249,7 @@ struct AttendArgs {
   const int64_t* dco; int32_t n_docs;
   const int32_t* sel_ids; const int32_t* n_sel; int32_t top_k;
   int64_t max_sel_chunks; int64_t pos0; double theta;
+  int32_t kv_on_host;             // K̄/V̄ are pinned host memory (read over PCIe)
   uint16_t* out; float* out_f32;
 };
 size_t attend_workspace(int32_t M, int32_t M_loc, int32_t n_q_heads, int64_t max_sel_chunks);
