@@ -74,6 +74,93 @@ def test_pool_chunk_size_and_long_doc():
         assert_pooled_close(u16(g), e, n)
 
 
+def test_pool_plain_means_are_exact():
+    """V̄ and K̄ᴿ carry no rotation. A chunk sum of bf16 values is exact in
+    fp64 for these data, and fp64 division is correctly rounded, so the GPU's
+    mean and the oracle's are the same double. After rounding to bf16 they
+    must be the same value, not merely within 1 ulp. This checks the GPU's
+    double -> bf16 rounding on every pooled value. ±0 compare equal."""
+    _banner("pool plain means exact (cfg1 + ragged)")
+    for mem in (synth.cfg1_tiny("cpu")[0],
+                synth.raw_memory([1, 2, 3, 63, 64, 65, 129, 1000, 7], 14, "cpu")):
+        Kb, Vb, Rb, dco_h, _ = _pool_gpu(mem)
+        oK, oV, oR, _ = O.pool(u16(mem.K), u16(mem.V), u16(mem.KR), mem.doc_token_offsets)
+        for g, e, n in ((Vb, oV, "V"), (Rb, oR, "KR")):
+            diff = O.bf16_ord(u16(g)) != O.bf16_ord(e)
+            assert not diff.any(), f"{n}: {int(diff.sum())} pooled values differ from the oracle"
+
+
+def _edge_tokens(rng, n_pairs):
+    """bf16 token pairs whose mean is a rounding edge case: neighbours (the
+    mean is a tie), 2^e and its lower neighbour (a tie whose even side is the
+    power of two), random pairs of one binade, bf16 subnormals, values next to
+    the largest finite bf16, and opposite signs (a zero mean)."""
+    kinds = rng.integers(0, 6, size=n_pairs)
+    a = np.empty(n_pairs, np.int64)
+    b = np.empty(n_pairs, np.int64)
+    for i, kind in enumerate(kinds):
+        sign = int(rng.integers(0, 2)) << 15
+        if kind == 0:                      # neighbours anywhere in the normal range
+            x = int(rng.integers(0x0080, 0x7F7F))
+            a[i], b[i] = x | sign, (x + 1) | sign
+        elif kind == 1:                    # a power of two and the value below it
+            e = int(rng.integers(2, 254))
+            a[i], b[i] = (e << 7) | sign, ((e << 7) - 1) | sign
+        elif kind == 2:                    # two values of one binade
+            e = int(rng.integers(1, 254))
+            a[i] = (e << 7) | int(rng.integers(0, 128)) | sign
+            b[i] = (e << 7) | int(rng.integers(0, 128)) | sign
+        elif kind == 3:                    # subnormals and the smallest normals
+            a[i] = int(rng.integers(1, 0x0100)) | sign
+            b[i] = int(rng.integers(1, 0x0100)) | sign
+        elif kind == 4:                    # the top of the finite range
+            a[i] = int(rng.integers(0x7F70, 0x7F80)) | sign
+            b[i] = int(rng.integers(0x7F70, 0x7F80)) | sign
+        else:                              # opposite signs of one value
+            x = int(rng.integers(1, 0x7F80))
+            a[i], b[i] = x, x | 0x8000
+    return a.astype(np.uint16), b.astype(np.uint16)
+
+
+@pytest.mark.parametrize("chunk", [2, 3])
+def test_pool_rounding_edge_values(chunk):
+    """Crafted tokens put the chunk means on bf16 rounding edges: ties between
+    neighbours, ties next to a power of two, subnormal means, means next to
+    the largest finite bf16, and zero. With chunk 3, each third token is a
+    copy of the first, so the mean is (2a + b) / 3: inexact, which exercises
+    the round-to-odd step. The pooled V̄ and K̄ᴿ must equal the oracle's
+    rounding (pinned to the definition) value for value."""
+    _banner(f"pool rounding edge values chunk={chunk}")
+    rng = np.random.default_rng(60 + chunk)
+    n_docs = 40
+    per = 2 * 8 * 128          # token pairs per document: both tensors' rows
+    lengths = [chunk] * n_docs
+    T = chunk * n_docs
+    V = np.empty((T, 8, 128), np.uint16)
+    R = np.empty((T, 8, 128), np.uint16)
+    for d in range(n_docs):
+        a, b = _edge_tokens(rng, per)
+        for dst, sl in ((V, slice(0, 1024)), (R, slice(1024, 2048))):
+            dst[d * chunk] = a[sl].reshape(8, 128)
+            dst[d * chunk + 1] = b[sl].reshape(8, 128)
+            if chunk == 3:
+                dst[d * chunk + 2] = a[sl].reshape(8, 128)
+    K = np.zeros_like(V)
+    to_t = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    mem = synth.RawMemory(to_t(K), to_t(V), to_t(R), synth.offsets_from_lengths(lengths))
+    d = msa.dims(chunk=chunk)
+    Kb, Vb, Rb, dco_h, _ = _pool_gpu(mem, d)
+    _, oV, oR, _ = O.pool(K, V, R, mem.doc_token_offsets, chunk=chunk)
+    for g, e, n in ((Vb, oV, "V"), (Rb, oR, "KR")):
+        got = u16(g)
+        diff = O.bf16_ord(got) != O.bf16_ord(e)
+        if diff.any():
+            i = np.flatnonzero(diff.ravel())[:4]
+            pytest.fail(f"{n}: {int(diff.sum())} values differ, e.g. got "
+                        f"{[hex(x) for x in got.ravel()[i]]} expected "
+                        f"{[hex(x) for x in e.ravel()[i]]}")
+
+
 def test_pool_deterministic():
     mem = synth.raw_memory([300, 77, 1024], 13, "cpu")
     a = _pool_gpu(mem)
@@ -295,6 +382,35 @@ def test_attend_k64_with_invalid_ids():
         sel_gpu.insert(pos, bad)
     assert len(sel_gpu) == 64
     _attend_case(2, 50, counts, valid, 79, pos0=64, top_k=64, sel_gpu=sel_gpu)
+
+
+@pytest.mark.parametrize("host_kv", [False, True])
+def test_attend_max_sel_truncates_the_selection(host_kv):
+    """max_sel_chunks below the selected documents' total: the memory part is
+    the first max_sel_chunks chunks in rank order (a cut inside a document),
+    still at pos0 = n_sel. The oracle attends over that prefix, assembled here
+    as a one-document store."""
+    _banner(f"attend max_sel truncation host_kv={host_kv}")
+    counts = [7, 12, 3, 20, 9, 5]
+    sel = [3, 1, 4, 0]                       # 20 + 12 + 9 + 7 = 48 chunks
+    max_sel = 30                             # cuts document 4 after 7 of its 9 chunks
+    st = synth.pooled_store(counts, 88, "cpu", with_kv=True)
+    att = synth.attend_inputs(5, 40, 88)
+    dco_h = st.doc_chunk_offsets
+    d = msa.dims(top_k=4)
+    sel_t = torch.tensor(sel, dtype=torch.int32, device=DEV)
+    ns_t = torch.tensor([4], dtype=torch.int32, device=DEV)
+    Kb, Vb = (st.Kbar.pin_memory(), st.Vbar.pin_memory()) if host_kv else \
+        (st.Kbar.to(DEV), st.Vbar.to(DEV))
+    out, of = msa.sparse_attend(att.Q.to(DEV), att.K_loc.to(DEV), att.V_loc.to(DEV), Kb, Vb,
+                                torch.from_numpy(dco_h).to(DEV), sel_t, ns_t, max_sel, d=d,
+                                want_f32=True)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(dco_h[i], dco_h[i + 1]) for i in sel])[:max_sel]
+    kb, vb = u16(st.Kbar)[rows], u16(st.Vbar)[rows]
+    ref = O.sparse_attend(u16(att.Q), u16(att.K_loc), u16(att.V_loc), kb, vb,
+                          np.array([0, max_sel]), [0], pos0=4)
+    assert_attn_close(of.cpu().numpy(), ref, "truncated selection")
 
 
 def test_attend_rejects_pageable_host_kv():

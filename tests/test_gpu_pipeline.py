@@ -1,13 +1,17 @@
 """Concurrent decode queries on separate streams (the pipelined form of the
 layer loop): each query's route → select → attend chain runs in order on its
-own stream while other queries' chains overlap it. Results must be bit-identical
-to running the same chains one after another on one stream."""
+own stream while other queries' chains overlap it. Every lane's document
+scores, selection and attention output are checked against the oracle, and
+the concurrent results must be bit-identical to running the same chains one
+after another on one stream."""
 import numpy as np
 import pytest
 import torch
 
 import routed_sparse_attention_amd as msa
 import synth
+from oracle import msa_oracle as O
+from tests._util import assert_attn_close, assert_scores_close, assert_topk_matches, u16
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -32,6 +36,7 @@ def test_concurrent_queries_match_sequential():
                      torch.empty((1,), dtype=torch.int32, device=DEV)),
             "out": [torch.empty((1, 32, 128), dtype=torch.bfloat16, device=DEV) for _ in range(L)],
             "ids": [None] * L,
+            "ds_l": [None] * L,
         }
 
     def layer(st, q, l):
@@ -40,6 +45,7 @@ def test_concurrent_queries_match_sequential():
         msa.route_scores(queries[ql].QR, store.KRbar[ql], d, out=st["S"])
         msa.select_topk(st["S"], dco, d, doc_scores=st["ds"], outs=st["outs"])
         st["ids"][l] = st["outs"][0].clone()
+        st["ds_l"][l] = st["ds"].clone()
         msa.sparse_attend(atts[ql].Q, atts[ql].K_loc, atts[ql].V_loc, store.Kbar, store.Vbar, dco,
                           st["outs"][0][0], st["outs"][2], max_sel, d=d, out=st["out"][l])
 
@@ -62,3 +68,25 @@ def test_concurrent_queries_match_sequential():
             assert torch.equal(seq[q]["out"][l].view(torch.int16), conc[q]["out"][l].view(torch.int16))
             ql = (l + q) % L
             assert set(queries[ql].planted_docs[0]) <= set(conc[q]["ids"][l][0].cpu().tolist())
+
+    # every lane against the oracle: document scores of all 30K chunks, the
+    # top-16 rule, and the decode attention over the lane's own selection
+    # read from pinned host memory
+    dco_h = store.doc_chunk_offsets
+    kb_h, vb_h = u16(store.Kbar), u16(store.Vbar)
+    oracle_s = {}
+    for ql in range(L):
+        oracle_s[ql] = O.doc_scores(O.chunk_scores(u16(queries[ql].QR[0]), u16(store.KRbar[ql])),
+                                    dco_h)
+    for q in range(Qn):
+        for l in range(L):
+            ql = (l + q) % L
+            ids = conc[q]["ids"][l][0].cpu().numpy()
+            assert_scores_close(conc[q]["ds_l"][l][0].cpu().numpy(), oracle_s[ql],
+                                f"lane {q} layer {l} doc scores")
+            assert_topk_matches(ids, 16, oracle_s[ql], 16)
+            a = atts[ql]
+            ref = O.sparse_attend(u16(a.Q), u16(a.K_loc), u16(a.V_loc), kb_h, vb_h, dco_h,
+                                  [int(x) for x in ids])
+            assert_attn_close(O.bf16_to_f64(u16(conc[q]["out"][l])), ref,
+                              f"lane {q} layer {l} attention")

@@ -55,6 +55,24 @@ MUTATIONS = {
     "aux_last_chunk_on_ties": ("j = int(np.argmax(seg))                          # first maximum",
                                "j = len(seg) - 1 - int(np.argmax(seg[::-1]))"),
     "aux_grad_not_divided_by_heads": ("g = ds[i] / H", "g = ds[i]"),
+    "bf16_ord_negatives_reversed": ("np.where(b & 0x8000, 0x8000 - b, b)",
+                                    "np.where(b & 0x8000, b - 0x8000, b)"),
+    "bf16_ord_negative_zero_apart": ("np.where(b & 0x8000, 0x8000 - b, b)",
+                                     "np.where(b & 0x8000, 0x7FFF - b, b)"),
+    "interleave_attends_new_tokens_only": (
+        "out = sparse_attend(Q_new, state.K_loc, state.V_loc, Kbar, Vbar, doc_chunk_offsets,",
+        "out = sparse_attend(Q_new, np.asarray(K_new), np.asarray(V_new), Kbar, Vbar, doc_chunk_offsets,"),
+    "interleave_keys_replaced_not_appended": (
+        "state.K_loc = np.concatenate([state.K_loc, np.asarray(K_new)], axis=0)",
+        "state.K_loc = np.asarray(K_new)"),
+    "aux_batched_key_grad_averaged": ("dK = np.sum([o[2] for o in outs], axis=0)",
+                                      "dK = np.mean([o[2] for o in outs], axis=0)"),
+    "aux_choice_ignored": ("            c, t = int(choice[0][i]), int(choice[1][i])",
+                           "            pass"),
+    "aux_choice_of_query_0_for_all": ("choice=None if choice is None else (choice[0][b], choice[1][b]))",
+                                      "choice=None if choice is None else (choice[0][0], choice[1][0]))"),
+    "aux_choice_keeps_free_score": ("s[i], c_star[i], t_star[i] = S[t, c], c, t",
+                                    "s[i], c_star[i], t_star[i] = Sc[c], c, t"),
 }
 
 # fast pins first: the loop stops at the first pin that fails

@@ -86,6 +86,31 @@ def test_bf16_roundtrip_all_patterns():
     assert np.array_equal(O.f64_to_bf16(vals[ok]), bits[ok])
 
 
+def test_bf16_ord_is_the_rank_of_the_value():
+    """bf16_ord, which the 1-ulp pooled criterion counts in, orders all
+    non-NaN patterns by value, ±0 share code 0, and neighbouring values differ
+    by exactly one code (so a code distance is a count of representable
+    values)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        vals = O.bf16_to_f64(bits)
+    ok = ~np.isnan(vals)
+    b, v = bits[ok], vals[ok]
+    code = O.bf16_ord(b).astype(np.int64)
+    order = np.argsort(v, kind="stable")
+    vs, cs = v[order], code[order]
+    step = np.diff(cs)
+    rises = np.diff(vs) > 0
+    assert np.array_equal(step[rises], np.ones(int(rises.sum()), np.int64))
+    assert np.array_equal(step[~rises], np.zeros(int((~rises).sum()), np.int64))
+    assert int(O.bf16_ord(np.uint16(0x0000))) == 0 == int(O.bf16_ord(np.uint16(0x8000)))
+    assert np.array_equal(np.sign(code), np.sign(v).astype(np.int64))
+    # hand values: 1.0 and the next bf16 above it; -1.0 and the next below it
+    assert int(O.bf16_ord(np.uint16(0x3F81)) - O.bf16_ord(np.uint16(0x3F80))) == 1
+    assert int(O.bf16_ord(np.uint16(0xBF80)) - O.bf16_ord(np.uint16(0xBF81))) == 1
+    assert int(O.bf16_ord(np.uint16(0x0001)) - O.bf16_ord(np.uint16(0x8001))) == 2
+
+
 def test_bf16_encode_matches_torch_on_float32():
     # torch rounds float32 -> bf16 to nearest-even in one step (library routine).
     x = (RNG.standard_normal(200_000) * np.exp(RNG.uniform(-30, 30, 200_000))).astype(np.float32)
@@ -490,6 +515,31 @@ def test_interleave_incremental_equals_full_reroute():
             assert out.shape == (96, 32, 128)
 
 
+def test_interleave_attends_over_the_whole_active_context():
+    """Each round's output is dense attention of the new tokens over every
+    pooled chunk (k >= N selects all documents, pos0 = N) plus *all* local
+    tokens appended so far, the new ones last and causal: checked against the
+    independent torch SDPA + complex-rotation reference, round by round."""
+    rng = np.random.default_rng(31)
+    counts = [2, 1, 3]
+    dco = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    C = int(dco[-1])
+    Kb, Vb = bf16_randn((C, 8, 128), 0.3, rng), bf16_randn((C, 8, 128), 0.3, rng)
+    Rb = bf16_randn((C, 8, 128), 0.125, rng)
+    st = O.InterleaveState(len(counts))
+    Ks, Vs = [], []
+    for r, m_new in enumerate((5, 3, 4)):
+        Q = bf16_randn((m_new, 32, 128), rng=rng)
+        Kn, Vn = bf16_randn((m_new, 8, 128), rng=rng), bf16_randn((m_new, 8, 128), rng=rng)
+        QR = bf16_randn((m_new, 8, 128), rng=rng)
+        Ks.append(Kn)
+        Vs.append(Vn)
+        ids, sc, mg, out = O.interleave_step(st, Q, Kn, Vn, QR, Rb, Kb, Vb, dco, k=4)
+        assert sorted(int(x) for x in ids) == [0, 1, 2]
+        ref = _dense_reference(Q, np.concatenate(Ks), np.concatenate(Vs), Kb, Vb, pos0=3)
+        assert np.allclose(out, ref, atol=1e-10, rtol=1e-10), f"round {r}"
+
+
 # ---------------------------------------------------------------------------
 # Router supervision: L_aux and its gradient ([techblg] §M training bullet)
 # ---------------------------------------------------------------------------
@@ -591,3 +641,96 @@ def test_aux_loss_subgradient_rules():
     _, dq, dk, s, cs, ts, gaps = O.aux_loss_f64(q, k, dco, [1], 0.1)
     assert cs[0] == 1 and ts[0] == 0 and gaps[0] == 0.0
     assert not dk[2].any() and not dq[1].any()
+
+
+def test_aux_batched_key_gradient_is_the_sum_over_queries():
+    """route_aux_loss over B queries: loss[b] and dQR[b] are query b's, and
+    dK̄ᴿ is the gradient of the summed loss — checked by central differences
+    of Σ_b loss_b in the keys (decoded bf16 values, perturbed in float64)."""
+    rng = np.random.default_rng(41)
+    dco = np.array([0, 2, 5, 6, 9], dtype=np.int64)
+    C = int(dco[-1])
+    KR = bf16_randn((C, 8, 128), 0.125, rng)
+    QR = bf16_randn((3, 2, 8, 128), rng=rng)
+    positives = [[1], [0, 3], [2]]
+    tau = 0.1
+    loss, dQ, dK, s, cs, ts, gaps = O.route_aux_loss(QR, KR, dco, positives, tau)
+    assert np.all(gaps > 1e-3)
+    k = O.bf16_to_f64(KR)
+    qs = [O.bf16_to_f64(QR[b]) for b in range(3)]
+    for b in range(3):
+        assert loss[b] == O.aux_loss_f64(qs[b], k, dco, positives[b], tau)[0]
+
+    def total(kk):
+        return sum(O.aux_loss_f64(qs[b], kk, dco, positives[b], tau)[0] for b in range(3))
+
+    h = 1e-6
+    # rows that carry gradient from more than one query are among those sampled
+    rows = sorted(set(int(c) for c in cs.ravel()))
+    for _ in range(30):
+        idx = (int(rng.choice(rows)), int(rng.integers(0, 8)), int(rng.integers(0, 128)))
+        old = k[idx]
+        k[idx] = old + h
+        fp = total(k)
+        k[idx] = old - h
+        fm = total(k)
+        k[idx] = old
+        fd = (fp - fm) / (2 * h)
+        assert abs(fd - dK[idx]) <= 1e-6 * max(1.0, abs(fd)), (idx, fd, dK[idx])
+    # each query's dQR is that query's own gradient
+    for b in range(3):
+        idx = (1, 4, 77)
+        q = qs[b]
+        old = q[idx]
+        q[idx] = old + h
+        fp = O.aux_loss_f64(q, k, dco, positives[b], tau)[0]
+        q[idx] = old - h
+        fm = O.aux_loss_f64(q, k, dco, positives[b], tau)[0]
+        q[idx] = old
+        assert abs((fp - fm) / (2 * h) - dQ[b][idx]) <= 1e-6
+
+
+def test_aux_choice_evaluates_at_the_given_pairs():
+    """``choice``: at the first maxima it reproduces the free call; at other
+    (chunk, token) pairs, s_i is the head-mean cosine at that pair and the
+    gradient is that of an independent torch forward that reads s_i there."""
+    rng = np.random.default_rng(43)
+    dco = np.array([0, 3, 4, 7], dtype=np.int64)
+    C = int(dco[-1])
+    KR = bf16_randn((C, 8, 128), 0.125, rng)
+    QR = bf16_randn((2, 3, 8, 128), rng=rng)
+    positives = [[2], [0]]
+    tau = 0.2
+    free = O.route_aux_loss(QR, KR, dco, positives, tau)
+    same = O.route_aux_loss(QR, KR, dco, positives, tau, choice=(free[4], free[5]))
+    for a, b in zip(free, same):
+        assert np.array_equal(a, b)
+    # other pairs: the last chunk of every document and token 2 (query 0),
+    # the first chunk and token 1 (query 1)
+    c_alt = np.stack([dco[1:] - 1, dco[:-1]])
+    t_alt = np.stack([np.full(3, 2), np.full(3, 1)])
+    loss, dQ, dK, s, cs, ts, _ = O.route_aux_loss(QR, KR, dco, positives, tau, choice=(c_alt, t_alt))
+    assert np.array_equal(cs, c_alt) and np.array_equal(ts, t_alt)
+    tk = torch.tensor(O.bf16_to_f64(KR), requires_grad=True)
+    kh = tk / tk.norm(dim=-1, keepdim=True).clamp_min(O.NORM_EPS)
+    total = 0.0
+    tqs = []
+    for b in range(2):
+        tq = torch.tensor(O.bf16_to_f64(QR[b]), requires_grad=True)
+        tqs.append(tq)
+        qh = tq / tq.norm(dim=-1, keepdim=True).clamp_min(O.NORM_EPS)
+        sb = torch.stack([(qh[int(t_alt[b, i])] * kh[int(c_alt[b, i])]).sum(-1).mean()
+                          for i in range(3)])
+        assert np.allclose(s[b], sb.detach().numpy(), rtol=0, atol=1e-15)
+        neg = torch.ones(3, dtype=torch.bool)
+        neg[positives[b]] = False
+        terms = [-(sb[i] / tau - torch.logsumexp(torch.cat([(sb[i] / tau).reshape(1),
+                                                            sb[neg] / tau]), 0))
+                 for i in positives[b]]
+        Lb = torch.stack(terms).mean()
+        assert abs(Lb.item() - loss[b]) < 1e-12
+        total = total + Lb
+    total.backward()
+    np.testing.assert_allclose(dK, tk.grad.numpy(), rtol=1e-9, atol=1e-12)
+    for b in range(2):
+        np.testing.assert_allclose(dQ[b], tqs[b].grad.numpy(), rtol=1e-9, atol=1e-12)
