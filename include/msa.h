@@ -32,7 +32,9 @@
  *     rejected.
  *   - The caller owns every buffer, including workspaces (sized by the
  *     *_workspace calls). The library keeps no allocation and no state across
- *     calls except the thread-local error string.
+ *     calls except the thread-local error string — and, for the one call
+ *     that takes no workspace (msa_route_topk_noalloc), a fixed device
+ *     scratch array per GPU and its looked-up address.
  *   - Inputs are never modified, except where a call says so.
  *   - bf16 tensors are raw bit patterns (msa_bf16), row-major and contiguous:
  *     token-major raw states [T, H, 128], pooled states [C, H, 128].
@@ -155,6 +157,31 @@ int32_t msa_route_topk(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t
                        int64_t n_chunks, float* doc_scores, int32_t accumulate, int32_t* topk_ids,
                        float* topk_scores, int32_t* n_sel, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* msa_route_topk without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Arguments, outputs and errors are those of
+ * msa_route_topk; the call allocates nothing.
+ *   Scratch: a fixed array of MSA_NOALLOC_SCRATCH_BYTES (16 MiB) in the
+ *     library's device memory, one per GPU, held until the process ends. That
+ *     covers msa_route_topk_workspace() up to 16 MiB — e.g. one single-token
+ *     query over 1,562,500 chunks (a 100M-token layer), or 64 single-token
+ *     queries over 60,000 chunks. A larger call returns MSA_ERR_WORKSPACE
+ *     before anything is enqueued.
+ *   Every call on one GPU uses the same scratch: calls that overlap on one GPU
+ *     (concurrent streams, or host threads) race and give wrong results;
+ *     order them on one stream or with events. The scratch keeps the last
+ *     call's contents, and nothing in it needs clearing between calls.
+ *   The stream must belong to the current device (MSA_ERR_INVALID_ARG
+ *     otherwise). The first call on a device looks up that device's scratch
+ *     address; that lookup and the library's error string are the only state
+ *     the library keeps across calls. */
+#define MSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int32_t msa_route_topk_noalloc(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
+                               const msa_bf16* KRbar, const int64_t* doc_chunk_offsets,
+                               int32_t n_docs, int64_t n_chunks, float* doc_scores,
+                               int32_t accumulate, int32_t* topk_ids, float* topk_scores,
+                               int32_t* n_sel, void* stream);
 
 /* The two halves of msa_route_topk, for callers that want the chunk scores
  * themselves (for instance to supervise routing) or to time the scan alone.

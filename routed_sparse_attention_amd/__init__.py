@@ -9,8 +9,8 @@ RoPE, GQA attention), ``Interleave`` (Memory Interleave rounds) and
 ``route_aux_loss`` (the router's auxiliary contrastive loss and its gradient).
 """
 from ._lib import (  # noqa: F401
-    DOC_ROPE_CHUNK, DOC_ROPE_TOKEN, EXPORTED, LIB_PATH, STORE_K, STORE_KR, STORE_V,
+    DOC_ROPE_CHUNK, DOC_ROPE_TOKEN, EXPORTED, LIB_PATH, NOALLOC_SCRATCH_BYTES, STORE_K, STORE_KR, STORE_V,
     TOKEN_REDUCE_MAX, TOKEN_REDUCE_MEAN, Dims, Interleave, MsaError, Store, dims, encode_pool,
-    lib, plan_chunks, route_aux_loss, route_topk, route_scores, route_topk_workspace, select_topk, sparse_attend,
+    lib, plan_chunks, route_aux_loss, route_topk, route_topk_noalloc, route_scores, route_topk_workspace, select_topk, sparse_attend,
     sparse_attend_workspace, store_file_info,
 )

@@ -30,8 +30,9 @@ EXPORTED = [
     "msa_sparse_attend_workspace", "msa_sparse_attend", "msa_interleave_reset",
     "msa_interleave_step_workspace", "msa_interleave_step", "msa_store_reset", "msa_store_append",
     "msa_store_save", "msa_store_load", "msa_store_file_info", "msa_route_aux_loss_workspace",
-    "msa_route_aux_loss",
+    "msa_route_aux_loss", "msa_route_topk_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 16 << 20   # MSA_NOALLOC_SCRATCH_BYTES
 STORE_KR, STORE_K, STORE_V = 1, 2, 4   # tensor bits of a store file
 
 
@@ -109,6 +110,8 @@ def lib() -> ctypes.CDLL:
         "msa_store_load": (_i32, [_DP, ctypes.POINTER(StoreC), ctypes.c_char_p, _vp, _sz]),
         "msa_store_file_info": (_i32, [ctypes.c_char_p, ctypes.POINTER(_i32), ctypes.POINTER(_i64),
                                        ctypes.POINTER(ctypes.c_uint32)]),
+        "msa_route_topk_noalloc": (_i32, [_DP, _vp, _i32, _i32, _vp, _vp, _i32, _i64, _vp, _i32,
+                                          _vp, _vp, _vp, _vp]),
         "msa_route_aux_loss_workspace": (_sz, [_DP, _i32, _i32, _i64, _i32]),
         "msa_route_aux_loss": (_i32, [_DP, _vp, _i32, _i32, _vp, _vp, _i32, _i64, _vp, _vp, _i32,
                                       ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -223,6 +226,33 @@ def route_topk(QR, KRbar, doc_chunk_offsets, d: Dims | None = None, doc_scores=N
     _check(lib().msa_route_topk(ctypes.byref(d), _p(QR), B, M, _p(KRbar), _p(doc_chunk_offsets),
                                 n_docs, C, _p(doc_scores), int(bool(accumulate)), _p(ids), _p(sc),
                                 _p(ns), _p(ws), ws.numel(), _stream()))
+    return doc_scores, ids, sc, ns
+
+
+def route_topk_noalloc(QR, KRbar, doc_chunk_offsets, d: Dims | None = None, doc_scores=None,
+                       accumulate: bool = False, outs=None):
+    """route_topk through the entry point that takes no workspace (the
+    library's fixed device scratch); the caller still passes the outputs."""
+    d = d or dims()
+    _need(QR, "QR", torch.bfloat16, ndim=4)
+    _need(KRbar, "KRbar", torch.bfloat16, ndim=3)
+    _need(doc_chunk_offsets, "doc_chunk_offsets", torch.int64)
+    B, M = QR.shape[0], QR.shape[1]
+    n_docs = doc_chunk_offsets.numel() - 1
+    dev = QR.device
+    if doc_scores is None:
+        if accumulate:
+            raise ValueError("accumulate needs doc_scores")
+        doc_scores = torch.empty((B, n_docs), dtype=torch.float32, device=dev)
+    if outs is None:
+        outs = (torch.empty((B, d.top_k), dtype=torch.int32, device=dev),
+                torch.empty((B, d.top_k), dtype=torch.float32, device=dev),
+                torch.empty((B,), dtype=torch.int32, device=dev))
+    ids, sc, ns = outs
+    _check(lib().msa_route_topk_noalloc(ctypes.byref(d), _p(QR), B, M, _p(KRbar),
+                                        _p(doc_chunk_offsets), n_docs, KRbar.shape[0],
+                                        _p(doc_scores), int(bool(accumulate)), _p(ids), _p(sc),
+                                        _p(ns), _stream()))
     return doc_scores, ids, sc, ns
 
 

@@ -125,6 +125,8 @@ int route_scores_impl(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t 
   return MSA_OK;
 }
 
+}  // namespace
+
 size_t route_topk_ws(int32_t B, int32_t M, int64_t C, int32_t N, int32_t K) {
   const ScanPlan p = scan_plan(B, M, C);
   const size_t sbytes = align_up((size_t)B * C * sizeof(float), 256);
@@ -166,6 +168,8 @@ int check_route_args(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M
     return fail(MSA_ERR_UNSUPPORTED, "route: accumulate needs the MAX token reduction");
   return MSA_OK;
 }
+
+namespace {
 
 int check_attend_args(const msa_dims* d, const msa_bf16* Q, int32_t M, const msa_bf16* K_loc,
                       const msa_bf16* V_loc, int32_t M_loc, const msa_bf16* Kbar,

@@ -241,6 +241,18 @@ int launch_doc_topk(const float* S, int32_t B, int64_t n_chunks, const int64_t* 
                     hipStream_t s);
 int launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 
+// Routing as one call (msa_route_topk): workspace bytes, argument checks and
+// the launches (scan, then document max and top-k); defined in msa_api.hip.
+size_t route_topk_ws(int32_t B, int32_t M, int64_t C, int32_t N, int32_t K);
+int check_route_args(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
+                     const msa_bf16* KRbar, const int64_t* dco, int32_t n_docs, int64_t n_chunks,
+                     const float* doc_scores, int32_t accumulate, const int32_t* topk_ids,
+                     const float* topk_scores, const int32_t* n_sel);
+int route_topk_impl(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
+                    const msa_bf16* KRbar, const int64_t* dco, int32_t n_docs, int64_t n_chunks,
+                    float* doc_scores, int32_t accumulate, int32_t* topk_ids, float* topk_scores,
+                    int32_t* n_sel, void* ws, size_t ws_bytes, hipStream_t s);
+
 // Sparse attention.
 struct AttendArgs {
   const uint16_t* Q; int32_t M; int32_t n_q_heads;

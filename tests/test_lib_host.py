@@ -175,3 +175,23 @@ def test_attend_workspace_covers_every_smaller_context():
                 w = msa.sparse_attend_workspace(M, M_loc, max_sel, d)
                 assert prev <= w <= top, (M, max_sel, M_loc)
                 prev = w
+
+
+def test_route_topk_noalloc_rejects_calls_beyond_its_scratch():
+    """The no-allocation routing call refuses, before touching the GPU, a
+    shape whose workspace exceeds its fixed scratch, and says how large each
+    is; other argument errors are those of msa_route_topk."""
+    L = msa.lib()
+    d = msa.dims()
+    p = ctypes.c_void_p(16)
+    C = 5_000_000                          # 20 MB of chunk scores for one query
+    need = msa.route_topk_workspace(1, 1, C, 1000, d)
+    assert need > msa.NOALLOC_SCRATCH_BYTES
+    rc = L.msa_route_topk_noalloc(ctypes.byref(d), p, 1, 1, p, p, 1000, C, p, 0, p, p, p, None)
+    assert rc == -3
+    msg = L.msa_last_error().decode()
+    assert str(need) in msg and str(msa.NOALLOC_SCRATCH_BYTES) in msg
+    rc = L.msa_route_topk_noalloc(ctypes.byref(d), None, 1, 1, p, p, 4, 8, p, 0, p, p, p, None)
+    assert rc == -1
+    rc = L.msa_route_topk_noalloc(ctypes.byref(d), p, 0, 1, p, p, 4, 8, p, 0, p, p, p, None)
+    assert rc == -2
