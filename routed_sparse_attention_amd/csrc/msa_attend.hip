@@ -527,30 +527,367 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   if (out_f32) out_f32[row * kDim + d] = o;
 }
 
+// ---------------------------------------------------------------------------
+// Multi-token queries (more than 32 query rows per KV head): one workgroup of
+// four waves per (128 query rows of one KV group, KV head, key split). The
+// waves share each 64-key tile of K and V, staged in LDS in two buffers (the
+// next tile's loads are in flight while the current one is multiplied), so a
+// tile is read from memory once per 128 rows instead of once per 32.
+//
+// Each wave computes S^T = K · Q^T for its 32 rows: the accumulator of
+// v_mfma_f32_32x32x16_bf16 then puts one query row in each lane (32 lanes ×
+// 2 halves), so the row maximum and sum need no cross-lane reduction beyond
+// one exchange between the halves, and the softmax weights P^T are already
+// laid out as the B operand of O^T += V^T · P^T: a lane's sixteen weights of
+// a 32-key block are keys 8a + 4·half + i (a = 0..3, i = 0..3). V^T is
+// stored in LDS with bits 2 and 3 of the key index swapped inside each
+// 16-key group, so that the A operand's eight keys per lane are contiguous
+// in that same order. O^T keeps one row per lane too, so the online-softmax
+// rescale is lane-local.
+//
+// Q and the local keys arrive rotated (rot_qk_kernel), so the tile loop has
+// no trigonometry. Partials (O, m, l per row and split) go to the workspace
+// in the layout combine_kernel reads.
+// ---------------------------------------------------------------------------
+constexpr int kMtWaves = 4;
+constexpr int kMtThreads = 64 * kMtWaves;
+constexpr int kMtRows = 32 * kMtWaves;          // query rows per workgroup
+constexpr int kMtKeys = 64;                     // keys per tile
+constexpr int kMtKPitch = 136;                  // bf16 per K row in LDS
+constexpr int kMtVPitch = 72;                   // bf16 per V^T row in LDS
+constexpr int kMtKElems = kMtKeys * kMtKPitch;
+constexpr int kMtVElems = kDim * kMtVPitch;
+constexpr int kMtBufElems = kMtKElems + kMtVElems;
+
+struct MtArgs {
+  const uint16_t* Qr; int32_t M; int32_t Hq;     // rotated queries [M, Hq, 128]
+  const uint16_t* Kr; const uint16_t* Vloc; int32_t M_loc;   // rotated local keys
+  const uint16_t* Kbar; const uint16_t* Vbar; int64_t n_chunks;
+  const int64_t* dco; int32_t n_docs;
+  const int32_t* sel_ids; const int32_t* n_sel; int32_t top_k;
+  int64_t max_sel;
+  int32_t key_split; float qk_scale_log2;
+  float* Opart; float* ML;
+};
+
+// Rotates the query rows (at pos0 + M_loc - M + u) and, when Kr != nullptr,
+// the local keys (at pos0 + v) into the workspace: one thread per rotation
+// pair, fp64 angle and sincos, bf16 result.
+__global__ __launch_bounds__(256) void rot_qk_kernel(const uint16_t* __restrict__ Q, int32_t M,
+                                                     int32_t Hq, const uint16_t* __restrict__ Kl,
+                                                     int32_t M_loc, const int32_t* __restrict__ n_sel,
+                                                     int32_t top_k, int64_t pos0_arg, RopeTab rt,
+                                                     uint16_t* __restrict__ Qr,
+                                                     uint16_t* __restrict__ Kr) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nq = (int64_t)M * Hq * (kDim / 2);
+  const int64_t nk = Kr ? (int64_t)M_loc * kHeads * (kDim / 2) : 0;
+  if (idx >= nq + nk) return;
+  const int64_t pos0 = pos0_arg < 0 ? (int64_t)clamp_nsel(n_sel, top_k) : pos0_arg;
+  const uint16_t* src;
+  uint16_t* dst;
+  int64_t row, pos;
+  int m;
+  if (idx < nq) {
+    row = idx / (kDim / 2);
+    m = (int)(idx % (kDim / 2));
+    pos = pos0 + (M_loc - M) + row / Hq;
+    src = Q;
+    dst = Qr;
+  } else {
+    const int64_t j = idx - nq;
+    row = j / (kDim / 2);
+    m = (int)(j % (kDim / 2));
+    pos = pos0 + row / kHeads;
+    src = Kl;
+    dst = Kr;
+  }
+  double sn, cs;
+  sincos((double)pos * rt.om[m], &sn, &cs);
+  const double x = bf16f(src[row * kDim + m]), y = bf16f(src[row * kDim + m + 64]);
+  dst[row * kDim + m] = d2bf(x * cs - y * sn);
+  dst[row * kDim + m + 64] = d2bf(y * cs + x * sn);
+}
+
+// LDS position of key q (0..63) of a tile in V^T: bits 2 and 3 swapped.
+__device__ __forceinline__ int vt_pos(int q) {
+  return (q & ~12) | ((q & 4) << 1) | ((q & 8) >> 1);
+}
+
+template <bool HOST_KV>
+__global__ __launch_bounds__(kMtThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_mt_kernel(const MtArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kMtBufElems];
+  __shared__ int32_t s_off[kMaxSel];
+  __shared__ int64_t s_start[kMaxSel];
+  __shared__ int32_t s_rows[2][kMtKeys];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int rg = blockIdx.x;
+  const int g = blockIdx.y;
+  const int split = blockIdx.z;
+  const int G = a.Hq / kHeads;
+  const int rows_g = a.M * G;
+  const int64_t n_rows_tot = (int64_t)a.M * a.Hq;
+  gbf16* Kbar = uniform_ptr(a.Kbar);
+  gbf16* Vbar = uniform_ptr(a.Vbar);
+  gbf16* Kloc = uniform_ptr(a.Kr);
+  gbf16* Vloc = uniform_ptr(a.Vloc);
+
+  // ---- this lane's query row (B operand of S^T = K Q^T): dims 16ks + 8·half
+  const int r = rg * kMtRows + wave * 32 + col;
+  const bool row_ok = r < rows_g;
+  const int u = row_ok ? r / G : 0;
+  const int hq = g * G + (row_ok ? r % G : 0);
+  uint4 qa[8];
+  {
+    const uint4* qrow = reinterpret_cast<const uint4*>(a.Qr + ((int64_t)u * a.Hq + hq) * kDim);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qa[ks] = row_ok ? qrow[ks * 2 + half] : make_uint4(0, 0, 0, 0);
+  }
+
+  // ---- chunk ranges of the selected documents in rank order (every wave
+  //      computes the prefix sum; wave 0 keeps it in LDS)
+  const int32_t id = lane < a.top_k ? a.sel_ids[lane] : -1;
+  const int ns = clamp_nsel(a.n_sel, a.top_k);
+  int64_t start = 0, cnt = 0;
+  if (lane < ns && id >= 0 && id < a.n_docs) {
+    int64_t c0 = a.dco[id], c1 = a.dco[id + 1];
+    c0 = max((int64_t)0, min(c0, a.n_chunks));
+    c1 = max(c0, min(c1, a.n_chunks));
+    start = c0;
+    cnt = c1 - c0;
+  }
+  int64_t incl = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  const int64_t total = __shfl(incl, 63);
+  const int n_mem = (int)min(total, a.max_sel);
+  if (wave == 0 && lane < ns) {
+    s_off[lane] = (int)min(incl - cnt, a.max_sel);
+    s_start[lane] = start;
+  }
+
+  // ---- keys of this split, cut where the workgroup's last token stops
+  //      seeing local keys (causal)
+  const int n_keys = n_mem + a.M_loc;
+  const int k_begin = split * a.key_split;
+  const int r_last = min(rows_g, (rg + 1) * kMtRows) - 1;
+  const int u_first = min(rg * kMtRows, rows_g - 1) / G;
+  const int lim_wg_hi = n_mem + (a.M_loc - a.M) + r_last / G;    // last key any row sees
+  const int lim_wg_lo = n_mem + (a.M_loc - a.M) + u_first;       // last key every row sees
+  const int k_end = min(min(k_begin + a.key_split, n_keys), lim_wg_hi + 1);
+  const int n_tiles = k_end > k_begin ? (k_end - k_begin + kMtKeys - 1) / kMtKeys : 0;
+  const int lim_row = n_mem + (a.M_loc - a.M) + u;               // last key this row sees
+
+  // key j of the context -> chunk row (>= 0) or -(v + 1) for local key v
+  auto key_row = [&](int j) -> int {
+    if (j < n_mem) {
+      int d = 0;
+#pragma unroll
+      for (int step = kMaxSel / 2; step > 0; step >>= 1) {
+        const int t = d + step;
+        if (t < ns && s_off[t] <= j) d = t;
+      }
+      return (int)(s_start[d] + (j - s_off[d]));
+    }
+    return -(j - n_mem + 1);
+  };
+
+  // loads of one tile: K as rows (lane (kq, dv): vector dv of keys kq + 16i),
+  // V as 8-dim slices of 4 consecutive keys (lane (c, dv): keys 4c .. 4c+3)
+  const int dv = tid & 15;
+  const int kq = tid >> 4;
+  u32x4 kx[4], vx[4];
+  auto load_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rk = s_rows[buf][kq + 16 * i];
+      const int64_t ok_ = rk >= 0 ? ((int64_t)rk * kHeads + g) * kDim
+                                  : ((int64_t)(-rk - 1) * kHeads + g) * kDim;
+      kx[i] = reinterpret_cast<gu32x4*>((rk >= 0 ? Kbar : Kloc) + ok_)[dv];
+      const int rv = s_rows[buf][4 * kq + i];
+      const int64_t ov = rv >= 0 ? ((int64_t)rv * kHeads + g) * kDim
+                                 : ((int64_t)(-rv - 1) * kHeads + g) * kDim;
+      vx[i] = reinterpret_cast<gu32x4*>((rv >= 0 ? Vbar : Vloc) + ov)[dv];
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* Ks = lds + buf * kMtBufElems;
+    uint16_t* Vt = Ks + kMtKElems;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(&Ks[(kq + 16 * i) * kMtKPitch + dv * 8]) = kx[i];
+    const int p0 = vt_pos(4 * kq);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = (e & 1) * 16;
+      const uint32_t w0 = ((vx[0][e >> 1] >> sh) & 0xffffu) | (((vx[1][e >> 1] >> sh) & 0xffffu) << 16);
+      const uint32_t w1 = ((vx[2][e >> 1] >> sh) & 0xffffu) | (((vx[3][e >> 1] >> sh) & 0xffffu) << 16);
+      *reinterpret_cast<uint2*>(&Vt[(dv * 8 + e) * kMtVPitch + p0]) = make_uint2(w0, w1);
+    }
+  };
+  auto rows_of = [&](int buf, int t) {
+    if (tid < kMtKeys) s_rows[buf][tid] = key_row(min(k_begin + t * kMtKeys + tid, k_end - 1));
+  };
+
+  f32x16_t O[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) O[db][v] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  __syncthreads();   // chunk list in LDS
+  if (n_tiles > 0) rows_of(0, 0);
+  __syncthreads();
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (n_tiles > 1) rows_of(1, 1);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int b = t & 1;
+    if (t + 1 < n_tiles) load_tile(b ^ 1);
+    const uint16_t* Ks = lds + b * kMtBufElems;
+    const uint16_t* Vt = Ks + kMtKElems;
+    const int tile0 = k_begin + t * kMtKeys;
+
+    // ---- S^T = K Q^T for the tile's two 32-key blocks
+    f32x16_t S[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) S[kb][v] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const uint4 ka =
+            *reinterpret_cast<const uint4*>(&Ks[(kb * 32 + col) * kMtKPitch + ks * 16 + half * 8]);
+        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qa[ks]), S[kb],
+                                                         0, 0, 0);
+      }
+    }
+
+    // ---- mask (only tiles that reach past the split's end or into keys
+    //      some row must not see), scale to the log2 domain, online softmax
+    const bool full = tile0 + kMtKeys <= k_end && tile0 + kMtKeys - 1 <= lim_wg_lo;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float sv = S[kb][v] * a.qk_scale_log2;
+        if (!full) {
+          const int j = tile0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          const bool ok = j < k_end && (j < n_mem || j <= lim_row);
+          sv = ok ? sv : -INFINITY;
+        }
+        S[kb][v] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const bool live = m_new != -INFINITY;
+    const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
+    float psum = 0.0f;
+    uint4 pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = live ? exp2f(S[kb][8 * sg + e] - m_new) : 0.0f;
+          psum += p[e];
+        }
+        pb[kb][sg] = pack8(p);
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) O[db][v] *= alpha;
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+          const uint4 va = *reinterpret_cast<const uint4*>(
+              &Vt[(db * 32 + col) * kMtVPitch + kb * 32 + sg * 16 + half * 8]);
+          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb[kb][sg]),
+                                                          O[db], 0, 0, 0);
+        }
+
+    if (t + 1 < n_tiles) {
+      store_tile(b ^ 1);
+      if (t + 2 < n_tiles) rows_of(b, t + 2);
+    }
+    __syncthreads();
+  }
+
+  // ---- partials: lane (row, half) holds dims 32db + 8a + 4·half + 0..3
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (row_ok) {
+    const int64_t grow = (int64_t)split * n_rows_tot + (int64_t)u * a.Hq + hq;
+    float* dst = a.Opart + grow * kDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(dst + db * 32 + 8 * q + 4 * half) =
+            make_float4(O[db][4 * q], O[db][4 * q + 1], O[db][4 * q + 2], O[db][4 * q + 3]);
+    if (half == 0) {
+      a.ML[grow * 2] = m_run;
+      a.ML[grow * 2 + 1] = l_tot;
+    }
+  }
+}
+
 struct AttnPlan {
+  bool multi;                 // the multi-token kernel (more than 32 rows per KV head)
   int32_t row_blocks, key_split, n_splits;
   bool rot_inline;
-  size_t off_kr, off_opart, off_ml, total;
+  size_t off_kr, off_qr, off_opart, off_ml, total;
 };
 
 AttnPlan attn_plan(int32_t M, int32_t M_loc, int32_t Hq, int64_t max_sel) {
   AttnPlan p;
   const int32_t G = Hq / kHeads;
-  p.row_blocks = (M * G + kRowTile - 1) / kRowTile;
+  const int32_t rows_g = M * G;
+  p.multi = rows_g > kRowTile;
+  const int32_t block_rows = p.multi ? kMtRows : kRowTile;
+  const int32_t tile_keys = p.multi ? kMtKeys : kKeyTile;
+  p.row_blocks = (rows_g + block_rows - 1) / block_rows;
   // with one row block every local key is read by one wave per KV head, so
-  // it is rotated where it is read; otherwise once, by rot_k_kernel
-  p.rot_inline = p.row_blocks == 1;
+  // it is rotated where it is read; otherwise once, by a rotation kernel
+  p.rot_inline = !p.multi && p.row_blocks == 1;
   const int64_t max_keys = max_sel + M_loc;
-  // aim for >= 2048 waves (8 per CU: one tile's loads of each in flight while
-  // the others compute), at most kMaxSplits splits
-  int64_t want = 2048 / ((int64_t)p.row_blocks * kHeads);
+  // one-wave kernel: aim for >= 2048 waves (8 per CU: one tile's loads of
+  // each in flight while the others compute); multi-token kernel: about two
+  // four-wave workgroups per CU. At most kMaxSplits splits either way.
+  const int64_t target = p.multi ? 512 : 2048;
+  int64_t want = target / ((int64_t)p.row_blocks * kHeads);
   if (want < 1) want = 1;
-  const int64_t tiles = (max_keys + kKeyTile - 1) / kKeyTile;
+  const int64_t tiles = (max_keys + tile_keys - 1) / tile_keys;
   int64_t tiles_per_split = (tiles + want - 1) / want;
   if (tiles_per_split < 1) tiles_per_split = 1;
   if ((tiles + tiles_per_split - 1) / tiles_per_split > kMaxSplits)
     tiles_per_split = (tiles + kMaxSplits - 1) / kMaxSplits;
-  p.key_split = (int32_t)(tiles_per_split * kKeyTile);
+  p.key_split = (int32_t)(tiles_per_split * tile_keys);
   p.n_splits = (int32_t)((max_keys + p.key_split - 1) / p.key_split);
   if (p.n_splits < 1) p.n_splits = 1;
   // The partials are sized for the most splits any key count up to max_keys
@@ -562,20 +899,17 @@ AttnPlan attn_plan(int32_t M, int32_t M_loc, int32_t Hq, int64_t max_sel) {
   if (ws_splits < p.n_splits) ws_splits = p.n_splits;
   size_t o = 0;
   p.off_kr = o; o = align_up(o + 2 * (size_t)M_loc * kHeads * kDim, 256);
+  p.off_qr = o; o = align_up(o + (p.multi ? 2 * (size_t)M * Hq * kDim : 0), 256);
   p.off_opart = o; o = align_up(o + 4 * (size_t)ws_splits * M * Hq * kDim, 256);
   p.off_ml = o; o = align_up(o + 4 * 2 * (size_t)ws_splits * M * Hq, 256);
   p.total = o;
   return p;
 }
 
-// omega_m = theta^(-2m/128), kept for the last theta used
-const RopeTab& rope_tab(double theta) {
-  static thread_local RopeTab t;
-  static thread_local double last = -1.0;
-  if (theta != last) {
-    for (int m = 0; m < kDim / 2; ++m) t.om[m] = std::pow(theta, -2.0 * (double)m / (double)kDim);
-    last = theta;
-  }
+// omega_m = theta^(-2m/128), made for each call
+RopeTab rope_tab(double theta) {
+  RopeTab t;
+  for (int m = 0; m < kDim / 2; ++m) t.om[m] = std::pow(theta, -2.0 * (double)m / (double)kDim);
   return t;
 }
 
@@ -590,34 +924,65 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s)
   if (ws_bytes < p.total) return fail(MSA_ERR_WORKSPACE, "attend workspace too small");
   char* base = static_cast<char*>(ws);
   uint16_t* Kr = reinterpret_cast<uint16_t*>(base + p.off_kr);
-  AttnArgs k;
-  k.Q = a.Q; k.M = a.M; k.Hq = a.n_q_heads;
-  k.Kloc = a.K_loc; k.Vloc = a.V_loc; k.M_loc = a.M_loc;
-  k.rot_inline = (!a.k_loc_rotated && p.rot_inline) ? 1 : 0;
-  k.Kbar = a.Kbar; k.Vbar = a.Vbar; k.n_chunks = a.n_chunks;
-  k.dco = a.dco; k.n_docs = a.n_docs;
-  k.sel_ids = a.sel_ids; k.n_sel = a.n_sel; k.top_k = a.top_k;
-  k.max_sel = a.max_sel_chunks; k.pos0 = a.pos0;
-  k.key_split = p.key_split;
-  k.qk_scale_log2 = (float)(1.0 / sqrt((double)kDim)) * kLog2e;
-  k.Opart = reinterpret_cast<float*>(base + p.off_opart);
-  k.ML = reinterpret_cast<float*>(base + p.off_ml);
-  k.rt = rope_tab(a.theta);
-  if (!a.k_loc_rotated && !p.rot_inline) {
-    const int64_t pairs = (int64_t)a.M_loc * kHeads * (kDim / 2);
-    hipLaunchKernelGGL(rot_k_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s,
-                       a.K_loc, a.M_loc, a.n_sel, a.top_k, a.pos0, k.rt, Kr);
-    MSA_LAUNCH_CHECK("rot_k_kernel launch");
-    k.Kloc = Kr;
+  float* Opart = reinterpret_cast<float*>(base + p.off_opart);
+  float* ML = reinterpret_cast<float*>(base + p.off_ml);
+  const float qk_scale_log2 = (float)(1.0 / sqrt((double)kDim)) * kLog2e;
+  const RopeTab rt = rope_tab(a.theta);
+
+  if (p.multi) {
+    uint16_t* Qr = reinterpret_cast<uint16_t*>(base + p.off_qr);
+    uint16_t* kr_dst = a.k_loc_rotated ? nullptr : Kr;
+    const int64_t pairs = ((int64_t)a.M * a.n_q_heads + (kr_dst ? (int64_t)a.M_loc * kHeads : 0)) *
+                          (kDim / 2);
+    hipLaunchKernelGGL(rot_qk_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s,
+                       a.Q, a.M, a.n_q_heads, a.K_loc, a.M_loc, a.n_sel, a.top_k, a.pos0, rt, Qr,
+                       kr_dst);
+    MSA_LAUNCH_CHECK("rot_qk_kernel launch");
+    MtArgs k;
+    k.Qr = Qr; k.M = a.M; k.Hq = a.n_q_heads;
+    k.Kr = a.k_loc_rotated ? a.K_loc : Kr; k.Vloc = a.V_loc; k.M_loc = a.M_loc;
+    k.Kbar = a.Kbar; k.Vbar = a.Vbar; k.n_chunks = a.n_chunks;
+    k.dco = a.dco; k.n_docs = a.n_docs;
+    k.sel_ids = a.sel_ids; k.n_sel = a.n_sel; k.top_k = a.top_k;
+    k.max_sel = a.max_sel_chunks;
+    k.key_split = p.key_split; k.qk_scale_log2 = qk_scale_log2;
+    k.Opart = Opart; k.ML = ML;
+    const dim3 grid(p.row_blocks, kHeads, p.n_splits);
+    if (a.kv_on_host)
+      hipLaunchKernelGGL(attn_mt_kernel<true>, grid, dim3(kMtThreads), 0, s, k);
+    else
+      hipLaunchKernelGGL(attn_mt_kernel<false>, grid, dim3(kMtThreads), 0, s, k);
+    MSA_LAUNCH_CHECK("attn_mt_kernel launch");
+  } else {
+    AttnArgs k;
+    k.Q = a.Q; k.M = a.M; k.Hq = a.n_q_heads;
+    k.Kloc = a.K_loc; k.Vloc = a.V_loc; k.M_loc = a.M_loc;
+    k.rot_inline = (!a.k_loc_rotated && p.rot_inline) ? 1 : 0;
+    k.Kbar = a.Kbar; k.Vbar = a.Vbar; k.n_chunks = a.n_chunks;
+    k.dco = a.dco; k.n_docs = a.n_docs;
+    k.sel_ids = a.sel_ids; k.n_sel = a.n_sel; k.top_k = a.top_k;
+    k.max_sel = a.max_sel_chunks; k.pos0 = a.pos0;
+    k.key_split = p.key_split;
+    k.qk_scale_log2 = qk_scale_log2;
+    k.Opart = Opart;
+    k.ML = ML;
+    k.rt = rt;
+    if (!a.k_loc_rotated && !p.rot_inline) {
+      const int64_t pairs = (int64_t)a.M_loc * kHeads * (kDim / 2);
+      hipLaunchKernelGGL(rot_k_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s,
+                         a.K_loc, a.M_loc, a.n_sel, a.top_k, a.pos0, k.rt, Kr);
+      MSA_LAUNCH_CHECK("rot_k_kernel launch");
+      k.Kloc = Kr;
+    }
+    if (a.kv_on_host)
+      hipLaunchKernelGGL(attn_kernel<true>, dim3(p.row_blocks, kHeads, p.n_splits), dim3(64), 0, s, k);
+    else
+      hipLaunchKernelGGL(attn_kernel<false>, dim3(p.row_blocks, kHeads, p.n_splits), dim3(64), 0, s, k);
+    MSA_LAUNCH_CHECK("attn_kernel launch");
   }
-  if (a.kv_on_host)
-    hipLaunchKernelGGL(attn_kernel<true>, dim3(p.row_blocks, kHeads, p.n_splits), dim3(64), 0, s, k);
-  else
-    hipLaunchKernelGGL(attn_kernel<false>, dim3(p.row_blocks, kHeads, p.n_splits), dim3(64), 0, s, k);
-  MSA_LAUNCH_CHECK("attn_kernel launch");
 
   const int64_t n_rows = (int64_t)a.M * a.n_q_heads;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)n_rows), dim3(kDim), 0, s, k.Opart, k.ML,
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)n_rows), dim3(kDim), 0, s, Opart, ML,
                      p.n_splits, n_rows, a.out, a.out_f32);
   MSA_LAUNCH_CHECK("combine_kernel launch");
   return MSA_OK;

@@ -230,6 +230,13 @@ int launch_scan_valu(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRb
                      int64_t n_chunks, int32_t token_reduce, float* out, hipStream_t s);
 int launch_scan_mfma(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRbar,
                      int64_t n_chunks, int32_t token_reduce, float* out, hipStream_t s);
+// Long queries (M >= kRowsScanMinTokens): q̂ rows in registers, key tiles
+// through LDS (msa_route_rows.hip). Queries over 128 rows write
+// scan_rows_parts(M) partials for launch_parts_combine.
+constexpr int kRowsScanMinTokens = 64;
+int32_t scan_rows_parts(int32_t M);
+int launch_scan_rows(const uint16_t* QR, int32_t B, int32_t M, const uint16_t* KRbar,
+                     int64_t n_chunks, int32_t token_reduce, float* out, hipStream_t s);
 int launch_parts_combine(const float* P, const RouteGeom& g, int64_t n_chunks,
                          int32_t token_reduce, float* S, hipStream_t s);
 

@@ -540,6 +540,41 @@ def test_route_ragged_chunk_counts(n_chunks, B, M):
     _check_route(QR, st, msa.dims())
 
 
+@pytest.mark.parametrize("n_chunks", [1, 31, 33, 3001])
+@pytest.mark.parametrize("B,M", [(1, 64), (2, 96), (1, 200), (3, 129)])
+def test_route_long_queries_ragged(n_chunks, B, M):
+    """The long-query scan (64 tokens or more: q̂ rows in registers, key tiles
+    through LDS): chunk counts that fill no tile or end mid-tile, queries that
+    are not whole 16-row blocks, several queries per workgroup, and queries
+    over 128 rows (per-part maxima folded by a second kernel)."""
+    _banner(f"route long n_chunks={n_chunks} B={B} M={M}")
+    st = _store(n_chunks, 700 + n_chunks, lo=1, hi=7)
+    QR = synth.randn_bf16((B, M, 8, 128), synth.torch_gen(11, n_chunks * 1000 + B * 300 + M))
+    _check_route(QR, st, msa.dims())
+
+
+@pytest.mark.parametrize("B,M", [(2, 300), (3, 70)])
+def test_route_long_queries_mean(B, M):
+    _banner(f"route long MEAN B={B} M={M}")
+    st = _store(2500, 33)
+    QR = synth.randn_bf16((B, M, 8, 128), synth.torch_gen(12, B * 1000 + M))
+    _check_route(QR, st, msa.dims(token_reduce=O.TOKEN_REDUCE_MEAN))
+
+
+def test_route_batched_rounds_accumulate():
+    """32 queries of 160 new tokens (two row groups each) routed in one call
+    and max-merged into their running scores: the batched form of an
+    interleave round, at a size the oracle redoes in seconds."""
+    _banner("route 32 queries x 160 tokens, accumulate")
+    st = _store(1000, 35, lo=2, hi=40)
+    d = msa.dims()
+    QR1 = synth.randn_bf16((32, 160, 8, 128), synth.torch_gen(13, 1))
+    QR2 = synth.randn_bf16((32, 160, 8, 128), synth.torch_gen(13, 2))
+    ds1, _, _ = _check_route(QR1, st, d)
+    # the running scores after round 1 (the GPU's, which both sides merge into)
+    _check_route(QR2, st, d, accumulate=True, prev=ds1.astype(np.float64))
+
+
 def _doc_scores_case(rng, case):
     """fp32 chunk scores for the threshold paths of the top-k select."""
     n_docs, k = {"bs128_nan": (3000, 16), "bs256_ragged": (20_000, 16), "wave_bs32": (2100, 40),
