@@ -538,16 +538,19 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
 // v_mfma_f32_32x32x16_bf16 then puts one query row in each lane (32 lanes ×
 // 2 halves), so the row maximum and sum need no cross-lane reduction beyond
 // one exchange between the halves, and the softmax weights P^T are already
-// laid out as the B operand of O^T += V^T · P^T: a lane's sixteen weights of
-// a 32-key block are keys 8a + 4·half + i (a = 0..3, i = 0..3). V^T is
-// stored in LDS with bits 2 and 3 of the key index swapped inside each
-// 16-key group, so that the A operand's eight keys per lane are contiguous
-// in that same order. O^T keeps one row per lane too, so the online-softmax
-// rescale is lane-local.
+// the B operand of O^T += V^T · P^T. For that, the sixteen weights a lane
+// holds for a 32-key block must be keys 16s + 8·half + 0..7 (s = 0, 1), so K
+// is stored in LDS with bits 2 and 3 of each key's row swapped; V^T keeps
+// the natural key order and is written with one 16-byte store per dim and 8
+// keys. O^T keeps one row per lane, so the online-softmax rescale is
+// lane-local, and it is skipped when no row maximum moved.
 //
-// Q and the local keys arrive rotated (rot_qk_kernel), so the tile loop has
-// no trigonometry. Partials (O, m, l per row and split) go to the workspace
-// in the layout combine_kernel reads.
+// Q arrives rotated and pre-scaled by log2(e)/sqrt(128) and the local keys
+// rotated (rot_qk_kernel), so the tile loop has no trigonometry. Each
+// workgroup writes its split's partial (O, m, l per row); combine_rows_kernel
+// merges the splits. (Merging in the last workgroup to finish would need a
+// device-scope release per workgroup, which on this chip writes back the
+// whole L2 of the workgroup's XCD: measured 3× slower than the extra pass.)
 // ---------------------------------------------------------------------------
 constexpr int kMtWaves = 4;
 constexpr int kMtThreads = 64 * kMtWaves;
@@ -560,24 +563,25 @@ constexpr int kMtVElems = kDim * kMtVPitch;
 constexpr int kMtBufElems = kMtKElems + kMtVElems;
 
 struct MtArgs {
-  const uint16_t* Qr; int32_t M; int32_t Hq;     // rotated queries [M, Hq, 128]
+  const uint16_t* Qr; int32_t M; int32_t Hq;     // rotated, pre-scaled queries [M, Hq, 128]
   const uint16_t* Kr; const uint16_t* Vloc; int32_t M_loc;   // rotated local keys
   const uint16_t* Kbar; const uint16_t* Vbar; int64_t n_chunks;
   const int64_t* dco; int32_t n_docs;
   const int32_t* sel_ids; const int32_t* n_sel; int32_t top_k;
   int64_t max_sel;
-  int32_t key_split; float qk_scale_log2;
+  int32_t key_split;
   float* Opart; float* ML;
 };
 
-// Rotates the query rows (at pos0 + M_loc - M + u) and, when Kr != nullptr,
-// the local keys (at pos0 + v) into the workspace: one thread per rotation
-// pair, fp64 angle and sincos, bf16 result.
+// Rotates the query rows (at pos0 + M_loc - M + u, then scaled by qscale) and,
+// when Kr != nullptr, the local keys (at pos0 + v) into the workspace: one
+// thread per rotation pair, the angle reduced to [-1/2, 1/2] revolutions in
+// fp64, hardware fp32 cos/sin, bf16 result.
 __global__ __launch_bounds__(256) void rot_qk_kernel(const uint16_t* __restrict__ Q, int32_t M,
                                                      int32_t Hq, const uint16_t* __restrict__ Kl,
                                                      int32_t M_loc, const int32_t* __restrict__ n_sel,
                                                      int32_t top_k, int64_t pos0_arg, RopeTab rt,
-                                                     uint16_t* __restrict__ Qr,
+                                                     float qscale, uint16_t* __restrict__ Qr,
                                                      uint16_t* __restrict__ Kr) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nq = (int64_t)M * Hq * (kDim / 2);
@@ -588,12 +592,14 @@ __global__ __launch_bounds__(256) void rot_qk_kernel(const uint16_t* __restrict_
   uint16_t* dst;
   int64_t row, pos;
   int m;
+  float sc = 1.0f;
   if (idx < nq) {
     row = idx / (kDim / 2);
     m = (int)(idx % (kDim / 2));
     pos = pos0 + (M_loc - M) + row / Hq;
     src = Q;
     dst = Qr;
+    sc = qscale;
   } else {
     const int64_t j = idx - nq;
     row = j / (kDim / 2);
@@ -602,15 +608,14 @@ __global__ __launch_bounds__(256) void rot_qk_kernel(const uint16_t* __restrict_
     src = Kl;
     dst = Kr;
   }
-  double sn, cs;
-  sincos((double)pos * rt.om[m], &sn, &cs);
-  const double x = bf16f(src[row * kDim + m]), y = bf16f(src[row * kDim + m + 64]);
-  dst[row * kDim + m] = d2bf(x * cs - y * sn);
-  dst[row * kDim + m + 64] = d2bf(y * cs + x * sn);
+  const float2 cs = cis_hw((double)pos * rt.om[m]);
+  const float x = bf16f(src[row * kDim + m]), y = bf16f(src[row * kDim + m + 64]);
+  dst[row * kDim + m] = f2bf((x * cs.x - y * cs.y) * sc);
+  dst[row * kDim + m + 64] = f2bf((y * cs.x + x * cs.y) * sc);
 }
 
-// LDS position of key q (0..63) of a tile in V^T: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int q) {
+// LDS row of key q (0..63) of a tile in the K buffer: bits 2 and 3 swapped.
+__device__ __forceinline__ int k_row(int q) {
   return (q & ~12) | ((q & 4) << 1) | ((q & 8) >> 1);
 }
 
@@ -701,37 +706,51 @@ void attn_mt_kernel(const MtArgs a) {
     return -(j - n_mem + 1);
   };
 
-  // loads of one tile: K as rows (lane (kq, dv): vector dv of keys kq + 16i),
-  // V as 8-dim slices of 4 consecutive keys (lane (c, dv): keys 4c .. 4c+3)
-  const int dv = tid & 15;
-  const int kq = tid >> 4;
-  u32x4 kx[4], vx[4];
+  // Loads of one tile: waves 0-1 read V as 8 consecutive keys × one 16-byte
+  // vector (lane (c, dv) = (t % 8, t / 8): keys 8c .. 8c + 7, vector dv), so
+  // each dim's 8 keys leave as one 16-byte V^T store; waves 2-3 read K rows
+  // (lane (q0, dv) = (t / 16, t % 16): keys q0 + 8i, vector dv). Either way
+  // each load instruction covers whole 128- or 256-byte runs of rows.
+  const bool is_v = wave < 2;
+  const int tt = tid & 127;
+  const int vc = tt & 7, vdv = tt >> 3;
+  const int kq0 = tt >> 4, kdv = tt & 15;
+  // this wave's two sources (pooled memory, local context) and lane vector
+  gbf16* const src_mem = is_v ? Vbar : Kbar;
+  gbf16* const src_loc = is_v ? Vloc : Kloc;
+  const int my_dv = is_v ? vdv : kdv;
+  const int q_base = is_v ? 8 * vc : kq0;
+  const int q_step = is_v ? 1 : 8;
+  u32x4 xv[8];
   auto load_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rk = s_rows[buf][kq + 16 * i];
-      const int64_t ok_ = rk >= 0 ? ((int64_t)rk * kHeads + g) * kDim
-                                  : ((int64_t)(-rk - 1) * kHeads + g) * kDim;
-      kx[i] = reinterpret_cast<gu32x4*>((rk >= 0 ? Kbar : Kloc) + ok_)[dv];
-      const int rv = s_rows[buf][4 * kq + i];
-      const int64_t ov = rv >= 0 ? ((int64_t)rv * kHeads + g) * kDim
-                                 : ((int64_t)(-rv - 1) * kHeads + g) * kDim;
-      vx[i] = reinterpret_cast<gu32x4*>((rv >= 0 ? Vbar : Vloc) + ov)[dv];
+    for (int i = 0; i < 8; ++i) {
+      const int rk = s_rows[buf][q_base + q_step * i];
+      const bool mem = rk >= 0;
+      const int64_t off = ((int64_t)(mem ? rk : -rk - 1) * kHeads + g) * kDim + my_dv * 8;
+      xv[i] = *reinterpret_cast<gu32x4*>((mem ? src_mem : src_loc) + off);
     }
   };
   auto store_tile = [&](int buf) {
     uint16_t* Ks = lds + buf * kMtBufElems;
     uint16_t* Vt = Ks + kMtKElems;
+    if (is_v) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(&Ks[(kq + 16 * i) * kMtKPitch + dv * 8]) = kx[i];
-    const int p0 = vt_pos(4 * kq);
+      for (int e = 0; e < 8; ++e) {
+        // dim vdv·8 + e of keys 8vc .. 8vc + 7
+        u32x4 w;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sh = (e & 1) * 16;
-      const uint32_t w0 = ((vx[0][e >> 1] >> sh) & 0xffffu) | (((vx[1][e >> 1] >> sh) & 0xffffu) << 16);
-      const uint32_t w1 = ((vx[2][e >> 1] >> sh) & 0xffffu) | (((vx[3][e >> 1] >> sh) & 0xffffu) << 16);
-      *reinterpret_cast<uint2*>(&Vt[(dv * 8 + e) * kMtVPitch + p0]) = make_uint2(w0, w1);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t wa = xv[2 * q][e >> 1];
+          const uint32_t wb = xv[2 * q + 1][e >> 1];
+          w[q] = (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
+        }
+        *reinterpret_cast<u32x4*>(&Vt[(vdv * 8 + e) * kMtVPitch + 8 * vc]) = w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(&Ks[k_row(kq0 + 8 * i) * kMtKPitch + kdv * 8]) = xv[i];
     }
   };
   auto rows_of = [&](int buf, int t) {
@@ -762,7 +781,8 @@ void attn_mt_kernel(const MtArgs a) {
     const uint16_t* Vt = Ks + kMtKElems;
     const int tile0 = k_begin + t * kMtKeys;
 
-    // ---- S^T = K Q^T for the tile's two 32-key blocks
+    // ---- S^T = K Q^T for the tile's two 32-key blocks (log2 domain: Q
+    //      carries the scale)
     f32x16_t S[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -778,26 +798,38 @@ void attn_mt_kernel(const MtArgs a) {
     }
 
     // ---- mask (only tiles that reach past the split's end or into keys
-    //      some row must not see), scale to the log2 domain, online softmax
+    //      some row must not see); register v of block kb holds key
+    //      32kb + 16(v / 8) + 8·half + v % 8
     const bool full = tile0 + kMtKeys <= k_end && tile0 + kMtKeys - 1 <= lim_wg_lo;
-    float mx = -INFINITY;
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = tile0 + kb * 32 + 16 * (v >> 3) + 8 * half + (v & 7);
+          const bool ok = j < k_end && (j < n_mem || j <= lim_row);
+          S[kb][v] = ok ? S[kb][v] : -INFINITY;
+        }
+    }
+    float mx = S[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float sv = S[kb][v] * a.qk_scale_log2;
-        if (!full) {
-          const int j = tile0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          const bool ok = j < k_end && (j < n_mem || j <= lim_row);
-          sv = ok ? sv : -INFINITY;
-        }
-        S[kb][v] = sv;
-        mx = fmaxf(mx, sv);
-      }
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kb][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
     const bool live = m_new != -INFINITY;
-    const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
+    // rescale only when some row's maximum moved (the common case after the
+    // first tiles is that none did)
+    if (__any(m_new != m_run)) {
+      const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) O[db][v] *= alpha;
+    }
+    m_run = m_new;
     float psum = 0.0f;
     uint4 pb[2][2];
 #pragma unroll
@@ -812,14 +844,9 @@ void attn_mt_kernel(const MtArgs a) {
         }
         pb[kb][sg] = pack8(p);
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) O[db][v] *= alpha;
+    l_run += psum;
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T: k-step (kb, sg) covers keys 32kb + 16sg + 8·half + 0..7
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -839,7 +866,7 @@ void attn_mt_kernel(const MtArgs a) {
     __syncthreads();
   }
 
-  // ---- partials: lane (row, half) holds dims 32db + 8a + 4·half + 0..3
+  // ---- this split's partial: lane (row, half) holds dims 32db + 8a + 4·half + 0..3
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (row_ok) {
     const int64_t grow = (int64_t)split * n_rows_tot + (int64_t)u * a.Hq + hq;
@@ -855,6 +882,42 @@ void attn_mt_kernel(const MtArgs a) {
       a.ML[grow * 2 + 1] = l_tot;
     }
   }
+}
+
+// Merges the key splits of the multi-token kernel: 32 threads per output
+// row, 4 dims each (16-byte loads of the partials); every split's (m, l) is
+// read first, then the partials are weighted by exp2(m_s - max) and summed in
+// split order.
+constexpr int kCombRows = 8;
+__global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restrict__ Opart,
+                                                           const float* __restrict__ ML,
+                                                           int32_t n_splits, int64_t n_rows,
+                                                           uint16_t* __restrict__ out,
+                                                           float* __restrict__ out_f32) {
+  const int64_t row = (int64_t)blockIdx.x * kCombRows + (threadIdx.x >> 5);
+  if (row >= n_rows) return;
+  const int d = (threadIdx.x & 31) * 4;
+  float mx = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, ML[((int64_t)s * n_rows + row) * 2]);
+  float L = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (mx != -INFINITY) {
+    for (int s = 0; s < n_splits; ++s) {
+      const int64_t gr = (int64_t)s * n_rows + row;
+      const float w = exp2f(ML[gr * 2] - mx);
+      L += w * ML[gr * 2 + 1];
+      const float4 x = *reinterpret_cast<const float4*>(Opart + gr * kDim + d);
+      acc.x += w * x.x;
+      acc.y += w * x.y;
+      acc.z += w * x.z;
+      acc.w += w * x.w;
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const float o[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+  *reinterpret_cast<uint2*>(out + row * kDim + d) =
+      make_uint2(pack2(f2bf(o[0]), f2bf(o[1])), pack2(f2bf(o[2]), f2bf(o[3])));
+  if (out_f32) *reinterpret_cast<float4*>(out_f32 + row * kDim + d) = make_float4(o[0], o[1], o[2], o[3]);
 }
 
 struct AttnPlan {
@@ -935,8 +998,8 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s)
     const int64_t pairs = ((int64_t)a.M * a.n_q_heads + (kr_dst ? (int64_t)a.M_loc * kHeads : 0)) *
                           (kDim / 2);
     hipLaunchKernelGGL(rot_qk_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s,
-                       a.Q, a.M, a.n_q_heads, a.K_loc, a.M_loc, a.n_sel, a.top_k, a.pos0, rt, Qr,
-                       kr_dst);
+                       a.Q, a.M, a.n_q_heads, a.K_loc, a.M_loc, a.n_sel, a.top_k, a.pos0, rt,
+                       qk_scale_log2, Qr, kr_dst);
     MSA_LAUNCH_CHECK("rot_qk_kernel launch");
     MtArgs k;
     k.Qr = Qr; k.M = a.M; k.Hq = a.n_q_heads;
@@ -945,7 +1008,7 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s)
     k.dco = a.dco; k.n_docs = a.n_docs;
     k.sel_ids = a.sel_ids; k.n_sel = a.n_sel; k.top_k = a.top_k;
     k.max_sel = a.max_sel_chunks;
-    k.key_split = p.key_split; k.qk_scale_log2 = qk_scale_log2;
+    k.key_split = p.key_split;
     k.Opart = Opart; k.ML = ML;
     const dim3 grid(p.row_blocks, kHeads, p.n_splits);
     if (a.kv_on_host)
@@ -953,6 +1016,11 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s)
     else
       hipLaunchKernelGGL(attn_mt_kernel<false>, grid, dim3(kMtThreads), 0, s, k);
     MSA_LAUNCH_CHECK("attn_mt_kernel launch");
+    const int64_t n_rows = (int64_t)a.M * a.n_q_heads;
+    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)((n_rows + kCombRows - 1) / kCombRows)),
+                       dim3(256), 0, s, Opart, ML, p.n_splits, n_rows, a.out, a.out_f32);
+    MSA_LAUNCH_CHECK("combine_rows_kernel launch");
+    return MSA_OK;
   } else {
     AttnArgs k;
     k.Q = a.Q; k.M = a.M; k.Hq = a.n_q_heads;
