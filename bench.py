@@ -19,6 +19,9 @@ value = memory tokens routed per second per query = 18 × 100M / step time.
 The JSON line also carries the roofline of the dominant kernel (the routing
 scan: 2048 algorithmic bytes per chunk, timed with HIP events around its own
 launches inside the timed region) and the CPU oracle timed on a bounded sample.
+Unless --no-sub is given, it also carries "sub_results" for the 16M batched
+routing, the 10M pooling and the 10M interleave workloads below, each with its
+own roofline and oracle baseline.
 
 Other workloads (--workload) measure single stages for the design notes:
   route16m    64 single-token queries against 250K pooled chunks (16M tokens):
@@ -61,6 +64,8 @@ def parse():
     ap.add_argument("--cpu-sample-chunks", type=int, default=400_000)
     ap.add_argument("--queries", type=int, default=2, help="concurrent queries (pipeline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="default workload only: skip the 16M, 10M-pool and interleave sub-results")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -467,9 +472,44 @@ def workload_pool10m(args):
 # ---------------------------------------------------------------------------
 # interleave: 32 queries × 3 rounds over a pooled 10M-token memory
 # ---------------------------------------------------------------------------
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def roofline_of(kernel, us, nbytes, flops, traffic=None):
+    """Roofline entry for one kernel: the bound is the resource whose floor
+    (bytes at 8 TB/s, flops at 2.5 PFLOP/s bf16) is the larger."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) if flops else 0.0
+    if t_mfma > t_hbm:
+        ach = flops / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "kernel": kernel, "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
+                "flops_per_launch": flops, "bytes_per_launch": nbytes,
+                "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    ach = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": ach, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
+            "bytes_per_launch": nbytes, "flops_per_launch": flops,
+            "mfma_frac": (flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS) if flops else None}
+
+
+def time_calls(fn, reps):
+    """Median µs of `reps` back-to-back calls of fn on the current stream."""
+    import numpy as np
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return float(np.median([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)]))
+
+
 def workload_interleave(args):
     import numpy as np
     import torch
+    from threadpoolctl import threadpool_limits
 
     import routed_sparse_attention_amd as msa
     import synth
@@ -510,8 +550,37 @@ def workload_interleave(args):
     torch.cuda.synchronize()
     found = sum(int(all(doc in set(states[qi].topk_ids.cpu().tolist()) for doc in chains[qi]))
                 for qi in range(n_q))
+    sel_chunks = int(sum(int(dco_h[i + 1] - dco_h[i]) for i in states[0].topk_ids.cpu().tolist()
+                         if i >= 0))
     tm = Timer()
     ms = run_timed(args, one_pass, tm)
+
+    # the two kernels of a round, timed alone on query 0's last round: the
+    # routing scan (256 tokens over the whole store) and the sparse attention
+    # (256 tokens over the selection and 768 local tokens)
+    QR, Q, Kn, Vn = rounds[0][n_r - 1]
+    S = torch.empty((1, C), dtype=torch.float32, device=dev)
+    rws = torch.empty(max(1, msa.lib().msa_route_scores_workspace(ctypes.byref(d), 1, 256, C)),
+                      dtype=torch.uint8, device=dev)
+    st0 = states[0]
+    K_loc = st0.K_loc[:st0.n_loc]
+    V_loc = st0.V_loc[:st0.n_loc]
+    aws = torch.empty(msa.sparse_attend_workspace(256, st0.n_loc, max_sel, d), dtype=torch.uint8,
+                      device=dev)
+    reps = max(10, args.steps)
+    scan_us = time_calls(lambda: msa.route_scores(QR[None], Rb, d, out=S, ws=rws), reps)
+    att_us = time_calls(lambda: msa.sparse_attend(Q, K_loc, V_loc, Kb, Vb, dco, st0.topk_ids,
+                                                  st0.n_sel, max_sel, d=d, ws=aws, out=out), reps)
+    scan_bytes = C * ROW_BYTES + C * 4          # keys once, one fp32 score per chunk
+    scan_flops = 2.0 * 256 * C * 1024
+    keys = sel_chunks + st0.n_loc
+    # K and V rows of every key (8 heads) once, Q read and the output written
+    att_bytes = keys * 8 * 128 * 2 * 2 + 256 * 32 * 128 * 2 * 2
+    att_flops = 4.0 * 256 * 32 * 128 * keys
+    roof_scan = roofline_of("scan_mfma_kernel + parts_combine_kernel (msa_route_scores, 256 tokens)", scan_us,
+                            scan_bytes, scan_flops)
+    roof_att = roofline_of("attn_mt_kernel (msa_sparse_attend, 256 tokens)", att_us,
+                           att_bytes, att_flops)
     tokens = C * TOKENS_PER_CHUNK
     routed = n_q * n_r * tokens
     r = base_result(args, "memory tokens routed/sec per query", routed / (ms * 1e-3), "tokens/s",
@@ -519,9 +588,46 @@ def workload_interleave(args):
                                      f"new tokens over a {tokens / 1e6:.1f}M-token pooled memory",
                          "queries": n_q, "rounds": n_r, "new_tokens_per_round": 256,
                          "memory_tokens": tokens, "chunks": C})
-    r.update({"round_us": tm.avg_us("round"),
+    r.update({"round_us": tm.avg_us("round"), "round_stats": tm.stats("round"),
               "queries_with_whole_chain_selected": f"{found}/{n_q}",
-              "roofline": None, "cpu_baseline": None})
+              "scan_us_256_tokens": scan_us, "attend_us_256x768": att_us,
+              "selected_chunks_query0": sel_chunks,
+              "roofline": roof_scan if scan_us >= att_us else roof_att,
+              "roofline_other": roof_att if scan_us >= att_us else roof_scan})
+    if not args.no_cpu_baseline:
+        from oracle import msa_oracle as O
+        # one query-round of the oracle: routing of the 256 tokens over a
+        # sample of the store (scaled to all chunks), and attention of a
+        # sample of the tokens over the round's selection (scaled to 256)
+        sample_c = 2_000
+        qr = u16(QR)
+        kr = u16(Rb[:sample_c])
+        kb_h, vb_h = u16(Kb), u16(Vb)
+        ids = [int(x) for x in st0.topk_ids.cpu().tolist() if x >= 0]
+        kl, vl, q_h = u16(K_loc), u16(V_loc), u16(Q)
+        toks = [0, 85, 170, 255]
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            O.chunk_scores(qr, kr)
+            t_route = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            for u in toks:
+                j = st0.n_loc - 256 + u
+                O.sparse_attend(q_h[u:u + 1], kl[:j + 1], vl[:j + 1], kb_h, vb_h, dco_h, ids,
+                                pos0=len(ids))
+            t_att = time.perf_counter() - t0
+        t_round = t_route * C / sample_c + t_att * 256 / len(toks)
+        r["cpu_baseline"] = {"value": tokens / t_round, "unit": "tokens/s", "cores": 1,
+                             "host_cores_available": host_cores(), "blas_threads": 1,
+                             "kind": "oracle",
+                             "sample": f"oracle interleave round of one query: routing of its 256 "
+                                       f"tokens over {sample_c:,} of {C:,} chunks ({t_route:.2f} s, "
+                                       f"scaled to the store) and attention of {len(toks)} of the "
+                                       f"256 tokens over its selection and local context "
+                                       f"({t_att:.2f} s, scaled to 256); numpy fp64, 1 thread",
+                             "seconds_measured": t_route + t_att}
+    else:
+        r["cpu_baseline"] = None
     return r
 
 
@@ -796,7 +902,23 @@ def main():
     fn = {"100m": workload_100m, "route16m": workload_route16m, "pool10m": workload_pool10m,
           "store": workload_store, "aux": workload_aux, "pipeline": workload_pipeline,
           "interleave": workload_interleave, "copy": workload_copy}[args.workload]
-    print(json.dumps(fn(args)), flush=True)
+    r = fn(args)
+    if args.workload == "100m" and not args.no_sub:
+        # the other measured workloads, each with its own roofline and oracle
+        # baseline, carried on the same line (the 100M store is freed first)
+        subs = {}
+        for name, sub in (("route_16m_batched", workload_route16m), ("pool_10m", workload_pool10m),
+                          ("interleave_10m", workload_interleave)):
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            log(args, f"sub-workload {name}")
+            x = sub(args)
+            for k in ("n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline",
+                      "dtype", "data"):
+                x.pop(k, None)
+            subs[name] = x
+        r["sub_results"] = subs
+    print(json.dumps(r), flush=True)
 
 
 if __name__ == "__main__":

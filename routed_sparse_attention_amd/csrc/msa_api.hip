@@ -90,32 +90,18 @@ int resolve_any(const void* p, const void** out, const char* name) {
 
 namespace {
 
-// Scan plan: kernel choice and the partials buffer needed when a query's
-// tokens span several row tiles. VALU for at most 8 query rows in all;
-// the long-query MFMA scan for queries of kRowsScanMinTokens tokens or more;
-// the batched MFMA scan for everything between.
-enum ScanKind { kScanValu, kScanMfma, kScanRows };
-
+// Scan plan: kernel choice (VALU for <= 8 query rows, MFMA above) and the
+// partials buffer needed when a query's tokens span several row tiles.
 struct ScanPlan {
-  ScanKind kind;
+  bool mfma;
   RouteGeom g;
   size_t parts_bytes;
 };
 
 ScanPlan scan_plan(int32_t B, int32_t M, int64_t C) {
   ScanPlan p;
-  if ((int64_t)B * M <= kValuTileRows) {
-    p.kind = kScanValu;
-    p.g = route_geom(B, M, kValuTileRows);
-  } else if (M >= kRowsScanMinTokens) {
-    p.kind = kScanRows;
-    p.g = route_geom(B, M, kMfmaTileRows);   // B and M for the combine
-    p.g.parts = scan_rows_parts(M);
-    p.g.n_tiles = 1;
-  } else {
-    p.kind = kScanMfma;
-    p.g = route_geom(B, M, kMfmaTileRows);
-  }
+  p.mfma = (int64_t)B * M > kValuTileRows;
+  p.g = route_geom(B, M, p.mfma ? kMfmaTileRows : kValuTileRows);
   p.parts_bytes = p.g.parts > 1 ? align_up((size_t)p.g.parts * B * C * sizeof(float), 256) : 0;
   return p;
 }
@@ -130,11 +116,8 @@ int route_scores_impl(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t 
     return fail(MSA_ERR_WORKSPACE, "route scores workspace: need %zu bytes, got %zu",
                 p.parts_bytes, ws_bytes);
   float* dst = p.g.parts > 1 ? static_cast<float*>(ws) : S;
-  int rc = p.kind == kScanRows
-               ? launch_scan_rows(QR, B, M, KRbar, n_chunks, d->token_reduce, dst, s)
-           : p.kind == kScanMfma
-               ? launch_scan_mfma(QR, p.g, KRbar, n_chunks, d->token_reduce, dst, s)
-               : launch_scan_valu(QR, p.g, KRbar, n_chunks, d->token_reduce, dst, s);
+  int rc = p.mfma ? launch_scan_mfma(QR, p.g, KRbar, n_chunks, d->token_reduce, dst, s)
+                  : launch_scan_valu(QR, p.g, KRbar, n_chunks, d->token_reduce, dst, s);
   if (rc) return rc;
   if (p.g.parts > 1) return launch_parts_combine(dst, p.g, n_chunks, d->token_reduce, S, s);
   return MSA_OK;

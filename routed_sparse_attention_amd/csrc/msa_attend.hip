@@ -148,8 +148,8 @@ __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
 }
 
 __device__ __forceinline__ uint4 pack8(const float* f) {
-  return make_uint4(pack2(f2bf(f[0]), f2bf(f[1])), pack2(f2bf(f[2]), f2bf(f[3])),
-                    pack2(f2bf(f[4]), f2bf(f[5])), pack2(f2bf(f[6]), f2bf(f[7])));
+  return make_uint4(cvt_pk_bf16(f[0], f[1]), cvt_pk_bf16(f[2], f[3]), cvt_pk_bf16(f[4], f[5]),
+                    cvt_pk_bf16(f[6], f[7]));
 }
 
 // LDS layout (bytes): K tile [32 keys][136] bf16, V^T tile [128 dims][40] bf16,

@@ -84,6 +84,16 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
   return (uint32_t)lo | ((uint32_t)hi << 16);
 }
 
+// Two floats -> packed bf16 pair with the hardware conversion (one
+// v_cvt_pk_bf16_f32, round to nearest even: the same bits as f2bf for every
+// non-NaN input; a NaN stays a NaN). For hot loops.
+typedef __bf16 msa_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float msa_f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const msa_f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, msa_bf16x2_t));
+}
+
 // Streaming 16-byte load that is not expected to be reused (non-temporal).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream(const uint4* p) {
@@ -229,13 +239,6 @@ constexpr int kMfmaTileRows = 16;   // one segment per MFMA lane group
 int launch_scan_valu(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRbar,
                      int64_t n_chunks, int32_t token_reduce, float* out, hipStream_t s);
 int launch_scan_mfma(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRbar,
-                     int64_t n_chunks, int32_t token_reduce, float* out, hipStream_t s);
-// Long queries (M >= kRowsScanMinTokens): q̂ rows in registers, key tiles
-// through LDS (msa_route_rows.hip). Queries over 128 rows write
-// scan_rows_parts(M) partials for launch_parts_combine.
-constexpr int kRowsScanMinTokens = 64;
-int32_t scan_rows_parts(int32_t M);
-int launch_scan_rows(const uint16_t* QR, int32_t B, int32_t M, const uint16_t* KRbar,
                      int64_t n_chunks, int32_t token_reduce, float* out, hipStream_t s);
 int launch_parts_combine(const float* P, const RouteGeom& g, int64_t n_chunks,
                          int32_t token_reduce, float* S, hipStream_t s);

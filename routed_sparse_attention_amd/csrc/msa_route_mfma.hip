@@ -320,11 +320,10 @@ int launch_scan_mfma(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRb
   if (wg < 1) wg = 1;
   const int64_t wg_max = (n_ct + kWaves - 1) / kWaves;
   if (wg > wg_max) wg = wg_max;
-  // more than 64 KiB of dynamic LDS has to be allowed once per process
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(scan_mfma_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)kLdsBytes);
-  if (attr != hipSuccess) return hip_fail(attr, "hipFuncSetAttribute(scan_mfma_kernel)");
+  // more than 64 KiB of dynamic LDS has to be allowed (set on every launch,
+  // so the library keeps no state between calls)
+  MSA_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(scan_mfma_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes));
   hipLaunchKernelGGL(scan_mfma_kernel, dim3((unsigned)wg, (unsigned)n_ty), dim3(kThreads),
                      kLdsBytes, s, QR, g, reinterpret_cast<const uint4*>(KRbar), n_chunks,
                      token_reduce, out);

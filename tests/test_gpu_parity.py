@@ -543,10 +543,10 @@ def test_route_ragged_chunk_counts(n_chunks, B, M):
 @pytest.mark.parametrize("n_chunks", [1, 31, 33, 3001])
 @pytest.mark.parametrize("B,M", [(1, 64), (2, 96), (1, 200), (3, 129)])
 def test_route_long_queries_ragged(n_chunks, B, M):
-    """The long-query scan (64 tokens or more: q̂ rows in registers, key tiles
-    through LDS): chunk counts that fill no tile or end mid-tile, queries that
-    are not whole 16-row blocks, several queries per workgroup, and queries
-    over 128 rows (per-part maxima folded by a second kernel)."""
+    """Long queries on the batched MFMA scan: chunk counts that fill no tile
+    or end mid-tile, queries that are not whole 16-row segments, several
+    queries per workgroup, and queries over 64 rows (per-part maxima folded
+    by a second kernel)."""
     _banner(f"route long n_chunks={n_chunks} B={B} M={M}")
     st = _store(n_chunks, 700 + n_chunks, lo=1, hi=7)
     QR = synth.randn_bf16((B, M, 8, 128), synth.torch_gen(11, n_chunks * 1000 + B * 300 + M))
@@ -562,7 +562,7 @@ def test_route_long_queries_mean(B, M):
 
 
 def test_route_batched_rounds_accumulate():
-    """32 queries of 160 new tokens (two row groups each) routed in one call
+    """32 queries of 160 new tokens (several row tiles each) routed in one call
     and max-merged into their running scores: the batched form of an
     interleave round, at a size the oracle redoes in seconds."""
     _banner("route 32 queries x 160 tokens, accumulate")
