@@ -28,7 +28,9 @@ Other workloads (--workload) measure single stages for the design notes:
               batched MFMA routing + top-16
   pool10m     Stage-1 pooling of 10M raw tokens (K, V, K^R, 61.4 GB read)
   interleave  3 Memory-Interleave rounds (256 new tokens each) for 32 queries
-              over a pooled 10M-token memory
+              over a pooled 10M-token memory; the queries advance together
+              (one batched routing scan per round), and the same rounds are
+              also timed one query at a time
   copy        a plain 2 GiB device-to-device copy: the known-size reference
               that scales the FETCH_SIZE / WRITE_SIZE counters into HBM bytes
 """
@@ -529,13 +531,38 @@ def workload_interleave(args):
     max_sel = d.top_k * int(np.diff(dco_h).max())
     n_q, n_r = len(chains), len(chains[0])
     n_docs = len(dco_h) - 1
+    # the 32 queries advance together: one batched routing scan per round
+    # (msa_interleave_batch_step), then each query's selection and attention
+    batch = msa.InterleaveBatch(n_q, n_docs, cap_loc=n_r * 256, d=d)
+    stacked = [tuple(torch.stack([rounds[qi][r][i] for qi in range(n_q)]) for i in range(4))
+               for r in range(n_r)]
+    bws = torch.empty(batch.workspace_bytes(256, C, max_sel), dtype=torch.uint8, device=dev)
+    bout = torch.empty((n_q, 256, 32, 128), dtype=torch.bfloat16, device=dev)
+
+    def one_pass(tm):
+        batch.reset()
+        for r in range(n_r):
+            QR, Q, Kn, Vn = stacked[r]
+            e0 = tm.ev() if tm else None
+            batch.step(Q, Kn, Vn, QR, Rb, Kb, Vb, dco, max_sel, ws=bws, out=bout)
+            if tm:
+                tm.add("round", e0, tm.ev())
+
+    one_pass(None)
+    torch.cuda.synchronize()
+    found = sum(int(all(doc in set(batch.topk_ids[qi].cpu().tolist()) for doc in chains[qi]))
+                for qi in range(n_q))
+    tm = Timer()
+    ms = run_timed(args, one_pass, tm)
+
+    # the same rounds one query at a time (msa_interleave_step), for comparison
     states = [msa.Interleave(n_docs, cap_loc=n_r * 256, d=d) for _ in range(n_q)]
     need = msa.lib().msa_interleave_step_workspace(ctypes.byref(d), 256, n_r * 256, C, n_docs,
                                                    max_sel)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     out = torch.empty((256, 32, 128), dtype=torch.bfloat16, device=dev)
 
-    def one_pass(tm):
+    def single_pass(tm):
         for qi in range(n_q):
             st = states[qi]
             st.reset()
@@ -544,16 +571,15 @@ def workload_interleave(args):
                 e0 = tm.ev() if tm else None
                 st.step(Q, Kn, Vn, QR, Rb, Kb, Vb, dco, max_sel, ws=ws, out=out)
                 if tm:
-                    tm.add("round", e0, tm.ev())
+                    tm.add("single", e0, tm.ev())
 
-    one_pass(None)
+    single_pass(None)
     torch.cuda.synchronize()
-    found = sum(int(all(doc in set(states[qi].topk_ids.cpu().tolist()) for doc in chains[qi]))
-                for qi in range(n_q))
+    same = all(torch.equal(states[qi].topk_ids, batch.topk_ids[qi]) for qi in range(n_q))
     sel_chunks = int(sum(int(dco_h[i + 1] - dco_h[i]) for i in states[0].topk_ids.cpu().tolist()
                          if i >= 0))
-    tm = Timer()
-    ms = run_timed(args, one_pass, tm)
+    tm_single = Timer()
+    single_ms = run_timed(args, single_pass, tm_single)
 
     # the two kernels of a round, timed alone on query 0's last round: the
     # routing scan (256 tokens over the whole store) and the sparse attention
@@ -569,6 +595,12 @@ def workload_interleave(args):
                       device=dev)
     reps = max(10, args.steps)
     scan_us = time_calls(lambda: msa.route_scores(QR[None], Rb, d, out=S, ws=rws), reps)
+    # the batched routing scan of one round (32 queries × 256 tokens)
+    QRb = stacked[n_r - 1][0]
+    Sb = torch.empty((n_q, C), dtype=torch.float32, device=dev)
+    rwsb = torch.empty(max(1, msa.lib().msa_route_scores_workspace(ctypes.byref(d), n_q, 256, C)),
+                       dtype=torch.uint8, device=dev)
+    scan_b_us = time_calls(lambda: msa.route_scores(QRb, Rb, d, out=Sb, ws=rwsb), max(3, reps // 3))
     att_us = time_calls(lambda: msa.sparse_attend(Q, K_loc, V_loc, Kb, Vb, dco, st0.topk_ids,
                                                   st0.n_sel, max_sel, d=d, ws=aws, out=out), reps)
     scan_bytes = C * ROW_BYTES + C * 4          # keys once, one fp32 score per chunk
@@ -577,10 +609,17 @@ def workload_interleave(args):
     # K and V rows of every key (8 heads) once, Q read and the output written
     att_bytes = keys * 8 * 128 * 2 * 2 + 256 * 32 * 128 * 2 * 2
     att_flops = 4.0 * 256 * 32 * 128 * keys
-    roof_scan = roofline_of("scan_mfma_kernel + parts_combine_kernel (msa_route_scores, 256 tokens)", scan_us,
-                            scan_bytes, scan_flops)
-    roof_att = roofline_of("attn_mt_kernel (msa_sparse_attend, 256 tokens)", att_us,
-                           att_bytes, att_flops)
+    scan_b_bytes = C * ROW_BYTES + n_q * C * 4
+    roof_scan = roofline_of("scan_mfma_kernel + parts_combine_kernel (msa_route_scores, "
+                            f"{n_q} queries × 256 tokens)", scan_b_us, scan_b_bytes,
+                            n_q * scan_flops,
+                            stored_traffic("interleave_scan", [csrc("msa_route_mfma.hip"),
+                                                               csrc("msa_route.hip"),
+                                                               csrc("msa_internal.h")]))
+    roof_att = roofline_of("rot_qk_kernel + attn_mt_kernel + combine_rows_kernel "
+                           "(msa_sparse_attend, 256 tokens)", att_us, att_bytes, att_flops,
+                           stored_traffic("interleave_attn", [csrc("msa_attend.hip"),
+                                                              csrc("msa_internal.h")]))
     tokens = C * TOKENS_PER_CHUNK
     routed = n_q * n_r * tokens
     r = base_result(args, "memory tokens routed/sec per query", routed / (ms * 1e-3), "tokens/s",
@@ -588,12 +627,17 @@ def workload_interleave(args):
                                      f"new tokens over a {tokens / 1e6:.1f}M-token pooled memory",
                          "queries": n_q, "rounds": n_r, "new_tokens_per_round": 256,
                          "memory_tokens": tokens, "chunks": C})
-    r.update({"round_us": tm.avg_us("round"), "round_stats": tm.stats("round"),
+    r.update({"batched_round_us": tm.avg_us("round"), "batched_round_stats": tm.stats("round"),
+              "round_us_per_query": tm.avg_us("round") / n_q,
+              "single_query_round_us": tm_single.avg_us("single"),
+              "single_query_round_stats": tm_single.stats("single"),
+              "single_query_pass_ms": single_ms,
+              "batched_selection_equals_single": same,
               "queries_with_whole_chain_selected": f"{found}/{n_q}",
-              "scan_us_256_tokens": scan_us, "attend_us_256x768": att_us,
-              "selected_chunks_query0": sel_chunks,
-              "roofline": roof_scan if scan_us >= att_us else roof_att,
-              "roofline_other": roof_att if scan_us >= att_us else roof_scan})
+              "scan_us_32x256_tokens": scan_b_us, "scan_us_256_tokens": scan_us,
+              "attend_us_256x768": att_us, "selected_chunks_query0": sel_chunks,
+              "roofline": roof_scan if scan_b_us >= n_q * att_us else roof_att,
+              "roofline_other": roof_att if scan_b_us >= n_q * att_us else roof_scan})
     if not args.no_cpu_baseline:
         from oracle import msa_oracle as O
         # one query-round of the oracle: routing of the 256 tokens over a
@@ -893,8 +937,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this MSA build measures one GPU; multi-GPU runs are not "
-                          "part of it (see the sharding notes in DESIGN.md)",
+        print(json.dumps({"error": "bench.py measures the MSA hot path on one GPU; runs on "
+                          "several GPUs are not supported",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     import torch

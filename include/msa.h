@@ -101,7 +101,7 @@ const char* msa_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
 int32_t msa_abi_version(void);
-#define MSA_ABI_VERSION 4
+#define MSA_ABI_VERSION 5
 
 /* ------------------------------------------------------------------------ */
 /* Chunk plan (host, pure). Each document is cut into ceil(n_i / chunk)
@@ -276,6 +276,54 @@ int32_t msa_interleave_step(const msa_dims* d, msa_interleave_state* st, const m
                             const int64_t* doc_chunk_offsets, int32_t n_docs,
                             int64_t max_sel_chunks, msa_bf16* out, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* Memory Interleave for B queries that advance together (same sections as
+ * above): one round routes the B queries' new tokens in one batched scan
+ * (each query max-merges into its own running document scores), re-selects
+ * each query's top-k and attends each query's new tokens over its own
+ * selection and local context. One scan launch covers every query's rows; the
+ * results equal B msa_interleave_step calls on the same inputs bit for bit
+ * when M_new > 8 (a single query of at most 8 rows takes the fp32-exact VALU
+ * scan instead, which may differ in the last bits). Buffers belong to the
+ * caller:
+ *   doc_scores [B, n_docs] fp32 (msa_interleave_batch_reset sets -inf);
+ *   K_loc, V_loc [B, cap_loc, n_kv_heads, 128] bf16, query b's rows at
+ *     b * cap_loc; every query holds n_loc tokens (host value, advanced by
+ *     M_new on success; MSA_ERR_SHAPE if n_loc + M_new > cap_loc);
+ *   topk_ids [B, top_k] int32, topk_scores [B, top_k] fp32, n_sel [B] int32:
+ *     this round's selections (written);
+ *   pos0: as in msa_sparse_attend, the same for every query (-1 means each
+ *     query's own n_sel).
+ * Step inputs: Q_new [B, M_new, n_q_heads, 128], K_new and V_new [B, M_new,
+ * n_kv_heads, 128], QR_new [B, M_new, n_router_heads, 128] bf16 (device); out
+ * [B, M_new, n_q_heads, 128] bf16 (written). ws / ws_bytes: at least
+ * msa_interleave_batch_step_workspace() bytes. On error nothing in the state
+ * has changed unless the message says the error came from a launch. */
+typedef struct msa_interleave_batch {
+  float* doc_scores;
+  msa_bf16* K_loc;
+  msa_bf16* V_loc;
+  int32_t B;
+  int32_t cap_loc;
+  int32_t n_loc;
+  int32_t* topk_ids;
+  float* topk_scores;
+  int32_t* n_sel;
+  int64_t pos0;
+} msa_interleave_batch;
+
+int32_t msa_interleave_batch_reset(msa_interleave_batch* st, int32_t n_docs, void* stream);
+size_t msa_interleave_batch_step_workspace(const msa_dims* d, int32_t B, int32_t M_new,
+                                           int32_t cap_loc, int64_t n_chunks, int32_t n_docs,
+                                           int64_t max_sel_chunks);
+int32_t msa_interleave_batch_step(const msa_dims* d, msa_interleave_batch* st,
+                                  const msa_bf16* Q_new, const msa_bf16* K_new,
+                                  const msa_bf16* V_new, const msa_bf16* QR_new, int32_t M_new,
+                                  const msa_bf16* KRbar, const msa_bf16* Kbar,
+                                  const msa_bf16* Vbar, int32_t kv_on_host, int64_t n_chunks,
+                                  const int64_t* doc_chunk_offsets, int32_t n_docs,
+                                  int64_t max_sel_chunks, msa_bf16* out, void* ws,
+                                  size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Router supervision: the auxiliary contrastive loss of the pages and its

@@ -30,7 +30,8 @@ EXPORTED = [
     "msa_sparse_attend_workspace", "msa_sparse_attend", "msa_interleave_reset",
     "msa_interleave_step_workspace", "msa_interleave_step", "msa_store_reset", "msa_store_append",
     "msa_store_save", "msa_store_load", "msa_store_file_info", "msa_route_aux_loss_workspace",
-    "msa_route_aux_loss", "msa_route_topk_noalloc",
+    "msa_route_aux_loss", "msa_route_topk_noalloc", "msa_interleave_batch_reset",
+    "msa_interleave_batch_step_workspace", "msa_interleave_batch_step",
 ]
 NOALLOC_SCRATCH_BYTES = 16 << 20   # MSA_NOALLOC_SCRATCH_BYTES
 STORE_KR, STORE_K, STORE_V = 1, 2, 4   # tensor bits of a store file
@@ -53,6 +54,14 @@ class Dims(ctypes.Structure):
 class InterleaveStateC(ctypes.Structure):
     _fields_ = [("doc_scores", ctypes.c_void_p), ("K_loc", ctypes.c_void_p),
                 ("V_loc", ctypes.c_void_p), ("cap_loc", ctypes.c_int32),
+                ("n_loc", ctypes.c_int32), ("topk_ids", ctypes.c_void_p),
+                ("topk_scores", ctypes.c_void_p), ("n_sel", ctypes.c_void_p),
+                ("pos0", ctypes.c_int64)]
+
+
+class InterleaveBatchC(ctypes.Structure):
+    _fields_ = [("doc_scores", ctypes.c_void_p), ("K_loc", ctypes.c_void_p),
+                ("V_loc", ctypes.c_void_p), ("B", ctypes.c_int32), ("cap_loc", ctypes.c_int32),
                 ("n_loc", ctypes.c_int32), ("topk_ids", ctypes.c_void_p),
                 ("topk_scores", ctypes.c_void_p), ("n_sel", ctypes.c_void_p),
                 ("pos0", ctypes.c_int64)]
@@ -103,6 +112,11 @@ def lib() -> ctypes.CDLL:
         "msa_interleave_step": (_i32, [_DP, ctypes.POINTER(InterleaveStateC), _vp, _vp, _vp, _vp,
                                        _i32, _vp, _vp, _vp, _i32, _i64, _vp, _i32, _i64, _vp, _vp,
                                        _sz, _vp]),
+        "msa_interleave_batch_reset": (_i32, [ctypes.POINTER(InterleaveBatchC), _i32, _vp]),
+        "msa_interleave_batch_step_workspace": (_sz, [_DP, _i32, _i32, _i32, _i64, _i32, _i64]),
+        "msa_interleave_batch_step": (_i32, [_DP, ctypes.POINTER(InterleaveBatchC), _vp, _vp, _vp,
+                                             _vp, _i32, _vp, _vp, _vp, _i32, _i64, _vp, _i32, _i64,
+                                             _vp, _vp, _sz, _vp]),
         "msa_store_reset": (_i32, [ctypes.POINTER(StoreC), _vp]),
         "msa_store_append": (_i32, [_DP, ctypes.POINTER(StoreC), _vp, _vp, _vp, _vp, _vp, _i32, _i64,
                                     _vp]),
@@ -386,6 +400,64 @@ class Interleave:
                                          _p(Kbar), _p(Vbar), int(on_host), KRbar.shape[0],
                                          _p(doc_chunk_offsets), self.n_docs, max_sel_chunks,
                                          _p(out), _p(ws), ws.numel(), _stream()))
+        return out
+
+
+class InterleaveBatch:
+    """Memory Interleave state for B queries that advance together
+    (msa_interleave_batch_*; caller-owned device buffers, contiguous per query)."""
+
+    def __init__(self, B: int, n_docs: int, cap_loc: int, device="cuda", d: Dims | None = None,
+                 pos0: int = -1):
+        self.d = d or dims()
+        self.B = B
+        self.n_docs = n_docs
+        self.doc_scores = torch.empty((B, n_docs), dtype=torch.float32, device=device)
+        self.K_loc = torch.zeros((B, cap_loc, 8, 128), dtype=torch.bfloat16, device=device)
+        self.V_loc = torch.zeros((B, cap_loc, 8, 128), dtype=torch.bfloat16, device=device)
+        self.topk_ids = torch.empty((B, self.d.top_k), dtype=torch.int32, device=device)
+        self.topk_scores = torch.empty((B, self.d.top_k), dtype=torch.float32, device=device)
+        self.n_sel = torch.empty((B,), dtype=torch.int32, device=device)
+        self.st = InterleaveBatchC(_p(self.doc_scores), _p(self.K_loc), _p(self.V_loc), B, cap_loc,
+                                   0, _p(self.topk_ids), _p(self.topk_scores), _p(self.n_sel), pos0)
+        self.reset()
+
+    def reset(self):
+        """Forget every round: running scores to -inf, no local tokens."""
+        _check(lib().msa_interleave_batch_reset(ctypes.byref(self.st), self.n_docs, _stream()))
+
+    @property
+    def n_loc(self) -> int:
+        return self.st.n_loc
+
+    def workspace_bytes(self, M_new: int, n_chunks: int, max_sel_chunks: int) -> int:
+        return lib().msa_interleave_batch_step_workspace(ctypes.byref(self.d), self.B, M_new,
+                                                         self.st.cap_loc, n_chunks, self.n_docs,
+                                                         max_sel_chunks)
+
+    def step(self, Q_new, K_new, V_new, QR_new, KRbar, Kbar, Vbar, doc_chunk_offsets,
+             max_sel_chunks: int, ws=None, out=None):
+        """One round: Q_new [B, M_new, n_q_heads, 128], K_new/V_new/QR_new
+        [B, M_new, 8, 128]; returns out [B, M_new, n_q_heads, 128]."""
+        d = self.d
+        for t, n in ((Q_new, "Q_new"), (K_new, "K_new"), (V_new, "V_new"), (QR_new, "QR_new")):
+            _need(t, n, torch.bfloat16, ndim=4)
+            if t.shape[0] != self.B:
+                raise ValueError(f"{n} has {t.shape[0]} queries, the state {self.B}")
+        _need(KRbar, "KRbar", torch.bfloat16, ndim=3)
+        on_host = Kbar.device.type == "cpu"
+        M_new = Q_new.shape[1]
+        dev = Q_new.device
+        if out is None:
+            out = torch.empty(Q_new.shape, dtype=torch.bfloat16, device=dev)
+        need = self.workspace_bytes(M_new, KRbar.shape[0], max_sel_chunks)
+        if ws is None or ws.numel() < need:
+            ws = _workspace(need, dev)
+        _check(lib().msa_interleave_batch_step(ctypes.byref(d), ctypes.byref(self.st), _p(Q_new),
+                                               _p(K_new), _p(V_new), _p(QR_new), M_new, _p(KRbar),
+                                               _p(Kbar), _p(Vbar), int(on_host), KRbar.shape[0],
+                                               _p(doc_chunk_offsets), self.n_docs, max_sel_chunks,
+                                               _p(out), _p(ws), ws.numel(), _stream()))
         return out
 
 

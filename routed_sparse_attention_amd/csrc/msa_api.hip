@@ -452,4 +452,98 @@ int32_t msa_interleave_step(const msa_dims* d, msa_interleave_state* st, const m
   return MSA_OK;
 }
 
+int32_t msa_interleave_batch_reset(msa_interleave_batch* st, int32_t n_docs, void* stream) {
+  clear_error();
+  if (!st || !st->doc_scores) return fail(MSA_ERR_INVALID_ARG, "interleave_batch_reset: NULL state");
+  if (n_docs < 1) return fail(MSA_ERR_SHAPE, "interleave_batch_reset: n_docs=%d must be >= 1", n_docs);
+  if (st->B < 1) return fail(MSA_ERR_SHAPE, "interleave_batch_reset: B=%d must be >= 1", st->B);
+  int rc = launch_fill_f32(st->doc_scores, (int64_t)st->B * n_docs, -INFINITY,
+                           static_cast<hipStream_t>(stream));
+  if (rc) return rc;
+  st->n_loc = 0;
+  return MSA_OK;
+}
+
+size_t msa_interleave_batch_step_workspace(const msa_dims* d, int32_t B, int32_t M_new,
+                                           int32_t cap_loc, int64_t n_chunks, int32_t n_docs,
+                                           int64_t max_sel_chunks) {
+  if (!d || B < 1 || M_new < 1 || cap_loc < M_new || n_chunks < 1 || n_docs < 1 ||
+      max_sel_chunks < 0)
+    return 0;
+  const size_t r = route_topk_ws(B, M_new, n_chunks, n_docs, d->top_k);
+  const size_t a = attend_workspace(M_new, cap_loc, d->n_q_heads, max_sel_chunks);
+  return r > a ? r : a;
+}
+
+int32_t msa_interleave_batch_step(const msa_dims* d, msa_interleave_batch* st,
+                                  const msa_bf16* Q_new, const msa_bf16* K_new,
+                                  const msa_bf16* V_new, const msa_bf16* QR_new, int32_t M_new,
+                                  const msa_bf16* KRbar, const msa_bf16* Kbar,
+                                  const msa_bf16* Vbar, int32_t kv_on_host, int64_t n_chunks,
+                                  const int64_t* dco, int32_t n_docs, int64_t max_sel_chunks,
+                                  msa_bf16* out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!st || !st->doc_scores || !st->K_loc || !st->V_loc || !st->topk_ids || !st->topk_scores ||
+      !st->n_sel)
+    return fail(MSA_ERR_INVALID_ARG, "interleave_batch: NULL state buffer");
+  if (!Q_new || !K_new || !V_new || !QR_new)
+    return fail(MSA_ERR_INVALID_ARG, "interleave_batch: NULL input");
+  const int32_t B = st->B;
+  if (B < 1) return fail(MSA_ERR_SHAPE, "interleave_batch: B=%d must be >= 1", B);
+  if (M_new < 1 || st->n_loc < 0 || (int64_t)st->n_loc + M_new > st->cap_loc)
+    return fail(MSA_ERR_SHAPE, "interleave_batch: n_loc (%d) + M_new (%d) exceeds cap_loc (%d)",
+                st->n_loc, M_new, st->cap_loc);
+  rc = check_route_args(d, QR_new, B, M_new, KRbar, dco, n_docs, n_chunks, st->doc_scores, 1,
+                        st->topk_ids, st->topk_scores, st->n_sel);
+  if (rc) return rc;
+  const int32_t M_loc = st->n_loc + M_new;
+  rc = check_attend_args(d, Q_new, M_new, st->K_loc, st->V_loc, M_loc, Kbar, Vbar, n_chunks, dco,
+                         n_docs, st->topk_ids, st->n_sel, max_sel_chunks, out);
+  if (rc) return rc;
+  const size_t need_r = route_topk_ws(B, M_new, n_chunks, n_docs, d->top_k);
+  const size_t need_a = attend_workspace(M_new, M_loc, d->n_q_heads, max_sel_chunks);
+  if (ws == nullptr || ws_bytes < need_r || ws_bytes < need_a)
+    return fail(MSA_ERR_WORKSPACE, "interleave_batch workspace too small");
+  const void* kb = nullptr;
+  const void* vb = nullptr;
+  rc = resolve_kv(Kbar, kv_on_host, &kb, "Kbar");
+  if (rc) return rc;
+  rc = resolve_kv(Vbar, kv_on_host, &vb, "Vbar");
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // one scan for all B queries (accumulating into each query's scores), then
+  // each query's attention; the attention calls reuse the workspace in
+  // stream order
+  rc = route_topk_impl(d, QR_new, B, M_new, KRbar, dco, n_docs, n_chunks, st->doc_scores, 1,
+                       st->topk_ids, st->topk_scores, st->n_sel, ws, ws_bytes, s);
+  if (rc) return rc;
+  const size_t row = (size_t)kRowElems;                       // elements per KV token row
+  const size_t q_row = (size_t)d->n_q_heads * kDim;           // elements per query token row
+  for (int32_t b = 0; b < B; ++b) {
+    msa_bf16* kl = st->K_loc + (size_t)b * st->cap_loc * row;
+    msa_bf16* vl = st->V_loc + (size_t)b * st->cap_loc * row;
+    MSA_HIP(hipMemcpyAsync(kl + (size_t)st->n_loc * row, K_new + (size_t)b * M_new * row,
+                           row * 2 * M_new, hipMemcpyDeviceToDevice, s));
+    MSA_HIP(hipMemcpyAsync(vl + (size_t)st->n_loc * row, V_new + (size_t)b * M_new * row,
+                           row * 2 * M_new, hipMemcpyDeviceToDevice, s));
+    AttendArgs a;
+    a.Q = Q_new + (size_t)b * M_new * q_row; a.M = M_new; a.n_q_heads = d->n_q_heads;
+    a.K_loc = kl; a.V_loc = vl; a.M_loc = M_loc; a.k_loc_rotated = 0;
+    a.Kbar = static_cast<const uint16_t*>(kb); a.Vbar = static_cast<const uint16_t*>(vb);
+    a.n_chunks = n_chunks; a.dco = dco; a.n_docs = n_docs;
+    a.sel_ids = st->topk_ids + (size_t)b * d->top_k; a.n_sel = st->n_sel + b;
+    a.top_k = d->top_k;
+    a.max_sel_chunks = max_sel_chunks; a.pos0 = st->pos0; a.theta = (double)d->rope_theta;
+    a.kv_on_host = kv_on_host ? 1 : 0;
+    a.out = out + (size_t)b * M_new * q_row; a.out_f32 = nullptr;
+    rc = launch_attend(a, ws, ws_bytes, s);
+    if (rc) return rc;
+  }
+  st->n_loc = M_loc;
+  return MSA_OK;
+}
+
 }  // extern "C"

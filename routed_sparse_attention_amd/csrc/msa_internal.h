@@ -39,7 +39,7 @@ int resolve_any(const void* p, const void** out, const char* name);
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Fixed head geometry of this build: 8 KV/router heads of dimension 128, so a
+// Fixed head geometry of this library: 8 KV/router heads of dimension 128, so a
 // token row of one tensor is 1024 bf16 = 2 KiB = 128 × 16-byte vectors.
 constexpr int kHeads = 8;
 constexpr int kDim = 128;

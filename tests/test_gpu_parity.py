@@ -448,6 +448,47 @@ def test_interleave_rounds():
     assert il.n_loc == 3 * 96
 
 
+def test_interleave_batch_equals_single_queries():
+    """Three queries advanced together through three rounds give, bit for
+    bit, what three single-query states give (one batched routing scan, then
+    each query's own selection and attention); query 1 is also checked
+    against the oracle."""
+    _banner("interleave batch of 3 queries, 3 rounds")
+    mem, chains = synth.cfg5_memory("cpu", seed=11, n_tokens=120_000, n_queries=3, hops=3)
+    Kb, Vb, Rb, dco_h, dco = _pool_gpu(mem)
+    oK, oV, oR, odco = O.pool(u16(mem.K), u16(mem.V), u16(mem.KR), mem.doc_token_offsets)
+    d = msa.dims(top_k=4)
+    max_sel = int(np.diff(dco_h).max()) * 4
+    n_docs = len(dco_h) - 1
+    B, M_new = 3, 96
+    batch = msa.InterleaveBatch(B, n_docs, cap_loc=3 * M_new, d=d)
+    singles = [msa.Interleave(n_docs, cap_loc=3 * M_new, d=d) for _ in range(B)]
+    st1 = O.InterleaveState(n_docs)
+    for r in range(3):
+        ins = [synth.cfg5_round(mem, chains[b][r], b, r, seed=11, M_new=M_new, block=64)
+               for b in range(B)]
+        QR, Q, Kn, Vn = (torch.stack([x[i] for x in ins]).to(DEV) for i in range(4))
+        out = batch.step(Q, Kn, Vn, QR, Rb, Kb, Vb, dco, max_sel)
+        outs = [singles[b].step(Q[b], Kn[b], Vn[b], QR[b], Rb, Kb, Vb, dco, max_sel)
+                for b in range(B)]
+        torch.cuda.synchronize()
+        for b in range(B):
+            assert torch.equal(batch.doc_scores[b], singles[b].doc_scores), (r, b)
+            assert torch.equal(batch.topk_ids[b], singles[b].topk_ids), (r, b)
+            assert torch.equal(batch.topk_scores[b], singles[b].topk_scores), (r, b)
+            assert torch.equal(batch.n_sel[b:b + 1], singles[b].n_sel), (r, b)
+            assert torch.equal(out[b], outs[b]), (r, b)
+            assert chains[b][r] in set(batch.topk_ids[b].cpu().numpy().tolist())
+        QR1, Q1, K1, V1 = ins[1]
+        ids, sc, mg, ref = O.interleave_step(st1, u16(Q1), u16(K1), u16(V1), u16(QR1), oR, oK, oV,
+                                             odco, k=4)
+        assert_scores_close(batch.doc_scores[1].cpu().numpy(), st1.doc_scores, f"round {r} doc scores")
+        assert_topk_matches(batch.topk_ids[1].cpu().numpy(), batch.n_sel.cpu().numpy()[1],
+                            st1.doc_scores, 4)
+        assert_attn_close(O.bf16_to_f64(u16(out[1])), ref, f"round {r} attention")
+    assert batch.n_loc == 3 * M_new
+
+
 # ---------------------------------------------------------------------------
 # boundary behaviour
 # ---------------------------------------------------------------------------

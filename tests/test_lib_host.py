@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = msa.lib()
     for name in _declared():
         assert hasattr(L, name), f"libmsa.so does not export {name}"
-    assert L.msa_abi_version() == 4
+    assert L.msa_abi_version() == 5
 
 
 def test_default_dims_follow_the_pages():
@@ -195,3 +195,26 @@ def test_route_topk_noalloc_rejects_calls_beyond_its_scratch():
     assert rc == -1
     rc = L.msa_route_topk_noalloc(ctypes.byref(d), p, 0, 1, p, p, 4, 8, p, 0, p, p, p, None)
     assert rc == -2
+
+
+def test_interleave_batch_rejects_bad_states_before_the_gpu():
+    """The batched interleave calls check the state and shapes on the host:
+    a batch of no queries, a round past the local capacity and missing
+    buffers fail with their codes and touch no device memory."""
+    L = msa.lib()
+    d = msa.dims()
+    p = ctypes.c_void_p(16)
+    st = msa._lib.InterleaveBatchC(p, p, p, 0, 64, 0, p, p, p, -1)
+    assert L.msa_interleave_batch_reset(ctypes.byref(st), 10, None) == -2
+    args = (p, p, p, p, 8, p, p, p, 0, 100, p, 10, 64, p, p, 1 << 20, None)
+    assert L.msa_interleave_batch_step(ctypes.byref(d), ctypes.byref(st), *args) == -2
+    st.B, st.n_loc = 2, 60                 # 60 + 8 tokens exceed cap_loc = 64
+    assert L.msa_interleave_batch_step(ctypes.byref(d), ctypes.byref(st), *args) == -2
+    assert b"cap_loc" in L.msa_last_error()
+    assert st.n_loc == 60
+    st.n_loc, st.doc_scores = 0, None
+    assert L.msa_interleave_batch_step(ctypes.byref(d), ctypes.byref(st), *args) == -1
+    assert L.msa_interleave_batch_step_workspace(ctypes.byref(d), 0, 8, 64, 100, 10, 64) == 0
+    one = L.msa_interleave_step_workspace(ctypes.byref(d), 8, 64, 100, 10, 64)
+    two = L.msa_interleave_batch_step_workspace(ctypes.byref(d), 2, 8, 64, 100, 10, 64)
+    assert two >= one > 0
