@@ -90,18 +90,32 @@ int resolve_any(const void* p, const void** out, const char* name) {
 
 namespace {
 
-// Scan plan: kernel choice (VALU for <= 8 query rows, MFMA above) and the
-// partials buffer needed when a query's tokens span several row tiles.
+// Scan plan: kernel choice and the workspace it needs. Queries whose token
+// count M is a multiple of 256 take the tiled contraction (msa_route_gemm.hip;
+// the choice depends on M alone, so a query gives the same scores alone or in
+// a batch); otherwise up to 8 rows in all take the VALU scan and more the
+// batched MFMA scan. A query whose rows span several row tiles needs the
+// partials buffer; the tiled scan also needs the normalised query rows.
+enum ScanKind { kScanValu, kScanMfma, kScanGemm };
 struct ScanPlan {
-  bool mfma;
+  ScanKind kind;
   RouteGeom g;
   size_t parts_bytes;
+  size_t qhat_bytes;
 };
 
 ScanPlan scan_plan(int32_t B, int32_t M, int64_t C) {
   ScanPlan p;
-  p.mfma = (int64_t)B * M > kValuTileRows;
-  p.g = route_geom(B, M, p.mfma ? kMfmaTileRows : kValuTileRows);
+  p.qhat_bytes = 0;
+  if (scan_gemm_fits(M)) {
+    p.kind = kScanGemm;
+    p.g = route_geom(B, M, M);                 // B, M; parts set below
+    p.g.parts = scan_gemm_parts(M);
+    p.qhat_bytes = scan_gemm_qhat_bytes(B, M);
+  } else {
+    p.kind = (int64_t)B * M > kValuTileRows ? kScanMfma : kScanValu;
+    p.g = route_geom(B, M, p.kind == kScanMfma ? kMfmaTileRows : kValuTileRows);
+  }
   p.parts_bytes = p.g.parts > 1 ? align_up((size_t)p.g.parts * B * C * sizeof(float), 256) : 0;
   return p;
 }
@@ -110,14 +124,22 @@ int route_scores_impl(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t 
                       const msa_bf16* KRbar, int64_t n_chunks, float* S, void* ws, size_t ws_bytes,
                       hipStream_t s) {
   const ScanPlan p = scan_plan(B, M, n_chunks);
-  if (p.g.n_tiles > 65535)
+  if (p.kind != kScanGemm && p.g.n_tiles > 65535)
     return fail(MSA_ERR_SHAPE, "route: %d row tiles exceed the grid limit (65535)", p.g.n_tiles);
-  if (ws_bytes < p.parts_bytes || (p.parts_bytes && ws == nullptr))
-    return fail(MSA_ERR_WORKSPACE, "route scores workspace: need %zu bytes, got %zu",
-                p.parts_bytes, ws_bytes);
+  const size_t need = p.parts_bytes + p.qhat_bytes;
+  if (ws_bytes < need || (need && ws == nullptr))
+    return fail(MSA_ERR_WORKSPACE, "route scores workspace: need %zu bytes, got %zu", need,
+                ws_bytes);
   float* dst = p.g.parts > 1 ? static_cast<float*>(ws) : S;
-  int rc = p.mfma ? launch_scan_mfma(QR, p.g, KRbar, n_chunks, d->token_reduce, dst, s)
-                  : launch_scan_valu(QR, p.g, KRbar, n_chunks, d->token_reduce, dst, s);
+  int rc;
+  if (p.kind == kScanGemm) {
+    uint16_t* qhat = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p.parts_bytes);
+    rc = launch_scan_gemm(QR, B, M, KRbar, n_chunks, d->token_reduce, dst, qhat, s);
+  } else if (p.kind == kScanMfma) {
+    rc = launch_scan_mfma(QR, p.g, KRbar, n_chunks, d->token_reduce, dst, s);
+  } else {
+    rc = launch_scan_valu(QR, p.g, KRbar, n_chunks, d->token_reduce, dst, s);
+  }
   if (rc) return rc;
   if (p.g.parts > 1) return launch_parts_combine(dst, p.g, n_chunks, d->token_reduce, S, s);
   return MSA_OK;
@@ -128,7 +150,7 @@ int route_scores_impl(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t 
 size_t route_topk_ws(int32_t B, int32_t M, int64_t C, int32_t N, int32_t K) {
   const ScanPlan p = scan_plan(B, M, C);
   const size_t sbytes = align_up((size_t)B * C * sizeof(float), 256);
-  return sbytes + p.parts_bytes + doc_topk_workspace(B, N, K);
+  return sbytes + p.parts_bytes + p.qhat_bytes + doc_topk_workspace(B, N, K);
 }
 
 int route_topk_impl(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
@@ -142,8 +164,9 @@ int route_topk_impl(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,
   char* base = static_cast<char*>(ws);
   const size_t sbytes = align_up((size_t)B * n_chunks * sizeof(float), 256);
   float* S = reinterpret_cast<float*>(base);
-  uint64_t* cand = reinterpret_cast<uint64_t*>(base + sbytes + p.parts_bytes);
-  int rc = route_scores_impl(d, QR, B, M, KRbar, n_chunks, S, base + sbytes, p.parts_bytes, s);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(base + sbytes + p.parts_bytes + p.qhat_bytes);
+  int rc = route_scores_impl(d, QR, B, M, KRbar, n_chunks, S, base + sbytes,
+                             p.parts_bytes + p.qhat_bytes, s);
   if (rc) return rc;
   return launch_doc_topk(S, B, n_chunks, dco, n_docs, doc_scores, accumulate, d->top_k, cand,
                          topk_ids, topk_scores, n_sel, s);
@@ -267,7 +290,8 @@ int32_t msa_encode_pool(const msa_dims* d, const msa_bf16* K, const msa_bf16* V,
 
 size_t msa_route_scores_workspace(const msa_dims* d, int32_t B, int32_t M, int64_t n_chunks) {
   if (!d || B < 1 || M < 1 || n_chunks < 1) return 0;
-  return scan_plan(B, M, n_chunks).parts_bytes;
+  const ScanPlan p = scan_plan(B, M, n_chunks);
+  return p.parts_bytes + p.qhat_bytes;
 }
 
 int32_t msa_route_scores(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M,

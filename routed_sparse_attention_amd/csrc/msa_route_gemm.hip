@@ -1,0 +1,318 @@
+// msa_route_score for long query blocks: the cosine scan as one tiled bf16
+// contraction over all router heads.
+//
+// Method (portal.techblg.uk IRMaD reading, section M, routing bullet):
+//   S_tc = mean_h cos(Q^R_{t,h}, K̄^R_{c,h}),  S_c = max_t S_tc (or mean_t).
+// With q̂ = q / max(‖q‖, eps) and k̂ = k / max(‖k‖, eps) per head, the head sum
+// of cosines is a plain sum of products over all 8 × 128 router dims, so a
+// query's scores are one [rows × 1024] · [1024 × chunks] product followed by
+// a max (or sum) over each query's rows (section M, Memory Parallel bullet:
+// the score matrix is computed in tiles and never held whole).
+//
+// Used when M is a multiple of 256 (every 256-row tile then belongs to one
+// query; a 128-token query would leave half of each tile's products unused).
+// Design:
+//   - qhat_rows_kernel writes q̂ once per call (fp64 norm per (row, head),
+//     the scaled value formed in fp32 and rounded to bf16);
+//   - scan_gemm_kernel: a workgroup of 8 waves owns 256 query rows × kCols
+//     chunks and walks the 8 heads as the contraction's k-steps (128 dims
+//     each). Each step's q̂ rows and key rows are staged through registers
+//     into LDS while the previous step's products run; the threads that stage
+//     a key row normalise it on the way (‖k‖ from the values they hold, a DPP
+//     sum over the 16 lanes sharing the row, then k̂ rounded to bf16). Rounding
+//     k̂ as well as q̂ to bf16 moves a score by ~1e-4 at most, inside the 1e-3
+//     score tolerance;
+//   - wave (wr, wc) computes rows 128·wr .. +128 × a quarter of the chunks with
+//     v_mfma_f32_32x32x16_bf16 (A = q̂ rows, B = k̂ rows, both read from LDS as
+//     one 16-byte fragment per lane; rows padded to 136 bf16 so the reads are
+//     bank-conflict free), accumulating all heads in one register tile;
+//   - epilogue: each wave reduces its 128 rows per chunk column (registers,
+//     then one exchange between the two lane halves) and the workgroup's two
+//     row halves are merged through LDS, so a 256-token query needs no second
+//     pass (longer queries write one partial per 256 rows);
+//   - workgroup order is XCD-aware: consecutive workgroups go to the 8 XCDs in
+//     turn, so workgroup L runs chunk tile (L % 8) + 8·(L / 8 / Y) for row tile
+//     (L / 8) % Y, and all Y row tiles of one chunk tile run together on one
+//     XCD, reading its key tile through one L2.
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kGWaves = 8;
+constexpr int kGThreads = 64 * kGWaves;
+constexpr int kGRows = 256;          // query rows per workgroup tile
+constexpr int kGPitch = 136;         // bf16 per LDS row (128 + 8: conflict-free fragment reads)
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// q̂ rows: one thread per (row, head), 128 dims. Same arithmetic as the
+// batched scan's staging: fp64 sum of squares, inv = 1 / max(‖q‖, eps)
+// rounded to fp32, q̂ = bf16(q · inv) formed in fp32.
+__global__ __launch_bounds__(256) void qhat_rows_kernel(const uint16_t* __restrict__ QR,
+                                                         int64_t n_rows, uint16_t* __restrict__ Qh) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // row * 8 + head
+  if (i >= n_rows * kHeads) return;
+  const uint4* src = reinterpret_cast<const uint4*>(QR) + i * (kDim / 8);
+  uint4 raw[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) raw[k] = src[k];
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = bf16lo(w[j]), b = bf16hi(w[j]);
+      ss += (double)(a * a) + (double)(b * b);
+    }
+  }
+  const double nrm = sqrt(ss);
+  const float inv = (float)(1.0 / (nrm > (double)kNormEps ? nrm : (double)kNormEps));
+  uint4* dst = reinterpret_cast<uint4*>(Qh) + i * (kDim / 8);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = pack2(f2bf(bf16lo(w[j]) * inv), f2bf(bf16hi(w[j]) * inv));
+    dst[k] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+struct GemmGeom {
+  int32_t B, M;
+  int64_t n_rows;        // B · M
+  int32_t n_row_tiles;   // n_rows / 256
+  int32_t n_col_tiles;   // ceil(n_chunks / kCols)
+  int32_t parts;         // 256-row tiles per query (1: final scores)
+};
+
+template <int kCols>
+__global__ __launch_bounds__(kGThreads) void scan_gemm_kernel(const uint16_t* __restrict__ Qh,
+                                                              GemmGeom g,
+                                                              const uint4* __restrict__ KR,
+                                                              int64_t n_chunks,
+                                                              int32_t token_reduce,
+                                                              float* __restrict__ out) {
+  constexpr int kNcb = kCols / 128;                 // 32-chunk column blocks per wave
+  constexpr int kBPass = kCols / 32;                // staging passes of the key tile
+  extern __shared__ uint4 lds4[];
+  uint16_t* As = reinterpret_cast<uint16_t*>(lds4);          // [256][kGPitch] q̂ of one head
+  uint16_t* Bs = As + kGRows * kGPitch;                       // [kCols][kGPitch] k̂ of one head
+
+  const int L = blockIdx.x;
+  const int Y = g.n_row_tiles;
+  const int slot = L >> 3;
+  const int x = (L & 7) + 8 * (slot / Y);   // chunk tile
+  const int y = slot % Y;                   // row tile
+  if (x >= g.n_col_tiles) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int wr = wave & 1;                  // row half
+  const int wc = wave >> 1;                 // column quarter
+
+  // staging: thread (r0, p) = (tid / 16, tid % 16) moves 16-byte piece p of
+  // rows r0 + 32·i; the 16 lanes of one row are one DPP row
+  const int p = tid & 15;
+  const int r0 = tid >> 4;
+  const int64_t c_base = (int64_t)x * kCols;
+  const int64_t row_base = (int64_t)y * kGRows;
+  // Each load is the tile's base (uniform) plus a 32-bit per-thread offset
+  // (a tile spans at most 512 KiB). Chunks past the end read the last chunk
+  // (clamped); their results are not stored.
+  constexpr int kRowV = kHeads * kDim / 8;                   // 16-byte vectors per row
+  const u32x4_t* qtile = reinterpret_cast<const u32x4_t*>(Qh) + row_base * kRowV;
+  const u32x4_t* ktile = reinterpret_cast<const u32x4_t*>(KR) + c_base * kRowV;
+  const int k_rows = (int)min((int64_t)kCols, n_chunks - c_base);   // >= 1
+  int koff[kBPass];
+#pragma unroll
+  for (int i = 0; i < kBPass; ++i) koff[i] = min(r0 + 32 * i, k_rows - 1) * kRowV + p;
+  u32x4_t qreg[8], kreg[kBPass];
+  auto load = [&](int h) {
+    const u32x4_t* qh = qtile + h * (kDim / 8);
+    const u32x4_t* kh = ktile + h * (kDim / 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qreg[i] = qh[(r0 + 32 * i) * kRowV + p];
+#pragma unroll
+    for (int i = 0; i < kBPass; ++i) kreg[i] = kh[koff[i]];
+  };
+  const float eps2 = kNormEps * kNormEps;
+  // k̂ = k / max(‖k‖, eps) per key row, in registers
+  auto normalise = [&]() {
+#pragma unroll
+    for (int i = 0; i < kBPass; ++i) {
+      const u32x4_t w = kreg[i];
+      float nk = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nk = dot2(w[j], w[j], nk);
+      const float inv = __builtin_amdgcn_rsqf(fmaxf(row_sum16(nk), eps2));
+      u32x4_t o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = cvt_pk_bf16(bf16lo(w[j]) * inv, bf16hi(w[j]) * inv);
+      kreg[i] = o;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4_t*>(As + (r0 + 32 * i) * kGPitch + p * 8) = qreg[i];
+#pragma unroll
+    for (int i = 0; i < kBPass; ++i)
+      *reinterpret_cast<u32x4_t*>(Bs + (r0 + 32 * i) * kGPitch + p * 8) = kreg[i];
+  };
+
+  f32x16_t acc[4][kNcb];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
+
+  load(0);
+  normalise();
+  store();
+  __syncthreads();
+
+  // fragment rows of this wave: A rows 128·wr + 32·rb + col, B rows
+  // (chunks) wc·(kCols/4) + 32·cb + col; k slice 16·ks + 8·half
+  const uint16_t* a_base = As + (wr * 128 + col) * kGPitch + half * 8;
+  const uint16_t* b_base = Bs + (wc * (kCols / 4) + col) * kGPitch + half * 8;
+
+  for (int h = 0; h < kHeads; ++h) {
+    if (h + 1 < kHeads) load(h + 1);
+#pragma unroll
+    for (int ks = 0; ks < kDim / 16; ++ks) {
+      // the next head's keys are normalised half way through this head's
+      // products, so their VALU work overlaps the MFMA pipeline
+      if (ks == kDim / 32 && h + 1 < kHeads) normalise();
+      u32x4_t a[4], b[kNcb];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        a[rb] = *reinterpret_cast<const u32x4_t*>(a_base + rb * 32 * kGPitch + ks * 16);
+#pragma unroll
+      for (int cb = 0; cb < kNcb; ++cb)
+        b[cb] = *reinterpret_cast<const u32x4_t*>(b_base + cb * 32 * kGPitch + ks * 16);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < kNcb; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[rb]), as_bf16x8(b[cb]),
+                                                                acc[rb][cb], 0, 0, 0);
+    }
+    __syncthreads();              // every wave is done with this head's tiles
+    if (h + 1 < kHeads) {
+      store();
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: reduce this wave's 128 rows per chunk column
+  const bool mean = token_reduce == MSA_TOKEN_REDUCE_MEAN;
+  float red[kNcb];
+#pragma unroll
+  for (int cb = 0; cb < kNcb; ++cb) {
+    float r = acc[0][cb][0];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        if (rb == 0 && v == 0) continue;
+        const float t = acc[rb][cb][v];
+        r = mean ? r + t : nan_max(r, t);
+      }
+    const float o = __shfl_xor(r, 32);
+    red[cb] = mean ? (half == 0 ? r + o : o + r) : (half == 0 ? nan_max(r, o) : nan_max(o, r));
+  }
+  // the two row halves are one query: half 1 hands its values to half 0,
+  // which writes the tile's part (query y / parts, part y % parts)
+  const float fin = (mean && g.parts == 1) ? 0.125f / (float)g.M : 0.125f;   // with the head mean
+  float* xch = reinterpret_cast<float*>(lds4);        // [4 column quarters][kNcb][32]
+  if (wr == 1 && half == 0) {
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb) xch[(wc * kNcb + cb) * 32 + col] = red[cb];
+  }
+  __syncthreads();
+  if (wr == 0 && half == 0) {
+    const int64_t b = y / g.parts, part = y % g.parts;
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb) {
+      const int64_t c = c_base + wc * (kCols / 4) + cb * 32 + col;
+      const float o = xch[(wc * kNcb + cb) * 32 + col];
+      if (c < n_chunks) out[(part * g.B + b) * n_chunks + c] = (mean ? red[cb] + o : nan_max(red[cb], o)) * fin;
+    }
+  }
+}
+
+template <int kCols>
+constexpr size_t gemm_lds_bytes() {
+  return (size_t)(kGRows + kCols) * kGPitch * 2;
+}
+
+}  // namespace
+
+bool scan_gemm_fits(int32_t M) { return M >= kGRows && M % kGRows == 0; }
+
+int32_t scan_gemm_parts(int32_t M) { return M / kGRows; }
+
+size_t scan_gemm_qhat_bytes(int32_t B, int32_t M) {
+  return align_up((size_t)B * M * kHeads * kDim * 2, 256);
+}
+
+int launch_scan_gemm(const uint16_t* QR, int32_t B, int32_t M, const uint16_t* KRbar,
+                     int64_t n_chunks, int32_t token_reduce, float* out, uint16_t* qhat,
+                     hipStream_t s) {
+  if (n_chunks == 0 || B == 0) return MSA_OK;
+  if (!scan_gemm_fits(M)) return fail(MSA_ERR_UNSUPPORTED, "tiled scan needs M a multiple of 256");
+  GemmGeom g;
+  g.B = B;
+  g.M = M;
+  g.n_rows = (int64_t)B * M;
+  if (g.n_rows / kGRows > 0x7fffffffLL) return fail(MSA_ERR_SHAPE, "tiled scan: too many rows");
+  g.n_row_tiles = (int32_t)(g.n_rows / kGRows);
+  g.parts = scan_gemm_parts(M);
+  const int64_t qthreads = g.n_rows * kHeads;
+  hipLaunchKernelGGL(qhat_rows_kernel, dim3((unsigned)((qthreads + 255) / 256)), dim3(256), 0, s,
+                     QR, g.n_rows, qhat);
+  MSA_LAUNCH_CHECK("qhat_rows_kernel launch");
+  // 256-chunk tiles when they give at least two workgroups per CU, else 128
+  const int64_t tiles256 = (n_chunks + 255) / 256;
+  const bool wide = tiles256 * g.n_row_tiles >= 512;
+  const int cols = wide ? 256 : 128;
+  g.n_col_tiles = (int32_t)((n_chunks + cols - 1) / cols);
+  const int64_t n_wg = 8 * (((int64_t)g.n_col_tiles + 7) / 8) * g.n_row_tiles;
+  if (n_wg > 0x7fffffffLL) return fail(MSA_ERR_SHAPE, "tiled scan: grid too large");
+  const uint4* kr = reinterpret_cast<const uint4*>(KRbar);
+  if (wide) {
+    MSA_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(scan_gemm_kernel<256>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)gemm_lds_bytes<256>()));
+    hipLaunchKernelGGL(scan_gemm_kernel<256>, dim3((unsigned)n_wg), dim3(kGThreads),
+                       gemm_lds_bytes<256>(), s, qhat, g, kr, n_chunks, token_reduce, out);
+  } else {
+    MSA_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(scan_gemm_kernel<128>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)gemm_lds_bytes<128>()));
+    hipLaunchKernelGGL(scan_gemm_kernel<128>, dim3((unsigned)n_wg), dim3(kGThreads),
+                       gemm_lds_bytes<128>(), s, qhat, g, kr, n_chunks, token_reduce, out);
+  }
+  MSA_LAUNCH_CHECK("scan_gemm_kernel launch");
+  return MSA_OK;
+}
+
+}  // namespace msa

@@ -602,6 +602,39 @@ def test_route_long_queries_mean(B, M):
     _check_route(QR, st, msa.dims(token_reduce=O.TOKEN_REDUCE_MEAN))
 
 
+@pytest.mark.parametrize("n_chunks", [1, 127, 129, 3001])
+@pytest.mark.parametrize("B,M", [(1, 256), (3, 256), (2, 512), (1, 768)])
+def test_route_tiled_scan(n_chunks, B, M):
+    """Queries of whole 256-token tiles take the tiled contraction scan: one
+    tile per query (the two row halves merged in the workgroup), and two or
+    three tiles per query folded by the second kernel, with chunk counts that
+    fill no 128- or 256-chunk tile or end mid-tile."""
+    _banner(f"route tiled n_chunks={n_chunks} B={B} M={M}")
+    st = _store(n_chunks, 900 + n_chunks, lo=1, hi=7)
+    QR = synth.randn_bf16((B, M, 8, 128), synth.torch_gen(14, n_chunks * 1000 + B * 300 + M))
+    _check_route(QR, st, msa.dims())
+
+
+@pytest.mark.parametrize("B,M", [(2, 256), (3, 512)])
+def test_route_tiled_scan_mean(B, M):
+    _banner(f"route tiled MEAN B={B} M={M}")
+    st = _store(2500, 37)
+    QR = synth.randn_bf16((B, M, 8, 128), synth.torch_gen(15, B * 1000 + M))
+    _check_route(QR, st, msa.dims(token_reduce=O.TOKEN_REDUCE_MEAN))
+
+
+def test_route_tiled_scan_rounds_accumulate():
+    """Eight queries of 256 new tokens (the interleave round shape) routed in
+    one call on the tiled scan and max-merged into their running scores."""
+    _banner("route 8 queries x 256 tokens, accumulate")
+    st = _store(1200, 38, lo=2, hi=40)
+    d = msa.dims()
+    QR1 = synth.randn_bf16((8, 256, 8, 128), synth.torch_gen(16, 1))
+    QR2 = synth.randn_bf16((8, 256, 8, 128), synth.torch_gen(16, 2))
+    ds1, _, _ = _check_route(QR1, st, d)
+    _check_route(QR2, st, d, accumulate=True, prev=ds1.astype(np.float64))
+
+
 def test_route_batched_rounds_accumulate():
     """32 queries of 160 new tokens (several row tiles each) routed in one call
     and max-merged into their running scores: the batched form of an
