@@ -30,10 +30,14 @@
 //     then one exchange between the two lane halves) and the workgroup's two
 //     row halves are merged through LDS, so a 256-token query needs no second
 //     pass (longer queries write one partial per 256 rows);
-//   - workgroup order is XCD-aware: consecutive workgroups go to the 8 XCDs in
-//     turn, so workgroup L runs chunk tile (L % 8) + 8·(L / 8 / Y) for row tile
-//     (L / 8) % Y, and all Y row tiles of one chunk tile run together on one
-//     XCD, reading its key tile through one L2.
+//   - workgroup order is XCD-aware (consecutive workgroups go to the 8 XCDs in
+//     turn). With 4 or more row tiles, each XCD runs blocks of 4 row tiles ×
+//     8 chunk tiles, 32 workgroups at a time, and its next block keeps the
+//     same row tiles while the eight XCDs walk the same chunk blocks: an XCD's
+//     q̂ rows stay in its L2 and each key block is fetched while all eight read
+//     it (32 queries × 256 tokens over 157K chunks: 10.4 → 3.8 GB of L2
+//     misses, 3.57 → 3.31 ms). With fewer row tiles, workgroup L runs chunk
+//     tile (L % 8) + 8·(L / 8 / Y) for row tile (L / 8) % Y.
 #include "msa_internal.h"
 
 namespace msa {
@@ -113,9 +117,21 @@ __global__ __launch_bounds__(kGThreads) void scan_gemm_kernel(const uint16_t* __
 
   const int L = blockIdx.x;
   const int Y = g.n_row_tiles;
-  const int slot = L >> 3;
-  const int x = (L & 7) + 8 * (slot / Y);   // chunk tile
-  const int y = slot % Y;                   // row tile
+  const int xcd = L & 7, slot = L >> 3;
+  int x, y;
+  if (Y >= 4) {
+    // blocks of 4 row tiles × 8 chunk tiles, one block per 32 consecutive
+    // workgroups of an XCD; an XCD's next block keeps its row tiles
+    const int blk = (slot >> 5) * 8 + xcd;
+    const int j = slot & 31;
+    const int RB = (Y + 3) / 4;
+    y = 4 * (blk % RB) + (j >> 3);
+    x = 8 * (blk / RB) + (j & 7);
+    if (y >= Y) return;
+  } else {
+    x = xcd + 8 * (slot / Y);   // chunk tile
+    y = slot % Y;               // row tile
+  }
   if (x >= g.n_col_tiles) return;
 
   const int tid = threadIdx.x;
@@ -295,7 +311,11 @@ int launch_scan_gemm(const uint16_t* QR, int32_t B, int32_t M, const uint16_t* K
   const bool wide = tiles256 * g.n_row_tiles >= 512;
   const int cols = wide ? 256 : 128;
   g.n_col_tiles = (int32_t)((n_chunks + cols - 1) / cols);
-  const int64_t n_wg = 8 * (((int64_t)g.n_col_tiles + 7) / 8) * g.n_row_tiles;
+  int64_t n_wg = 8 * (((int64_t)g.n_col_tiles + 7) / 8) * g.n_row_tiles;
+  if (g.n_row_tiles >= 4) {
+    const int64_t blocks = (((int64_t)g.n_row_tiles + 3) / 4) * (((int64_t)g.n_col_tiles + 7) / 8);
+    n_wg = 8 * 32 * ((blocks + 7) / 8);
+  }
   if (n_wg > 0x7fffffffLL) return fail(MSA_ERR_SHAPE, "tiled scan: grid too large");
   const uint4* kr = reinterpret_cast<const uint4*>(KRbar);
   if (wide) {
