@@ -488,6 +488,21 @@ int32_t msa_interleave_batch_reset(msa_interleave_batch* st, int32_t n_docs, voi
   return MSA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+// Queries of a batched interleave round attended per set of launches: up to
+// kAttendGroup when the multi-token kernel serves the shape (their partials
+// share the workspace), else one.
+constexpr int32_t kAttendGroup = 8;
+int32_t attend_group(int32_t B, int32_t M_new, int32_t n_q_heads) {
+  if (!attend_is_multi(M_new, n_q_heads)) return 1;
+  return B < kAttendGroup ? B : kAttendGroup;
+}
+}  // namespace
+
+extern "C" {
+
 size_t msa_interleave_batch_step_workspace(const msa_dims* d, int32_t B, int32_t M_new,
                                            int32_t cap_loc, int64_t n_chunks, int32_t n_docs,
                                            int64_t max_sel_chunks) {
@@ -495,7 +510,8 @@ size_t msa_interleave_batch_step_workspace(const msa_dims* d, int32_t B, int32_t
       max_sel_chunks < 0)
     return 0;
   const size_t r = route_topk_ws(B, M_new, n_chunks, n_docs, d->top_k);
-  const size_t a = attend_workspace(M_new, cap_loc, d->n_q_heads, max_sel_chunks);
+  const size_t a = attend_workspace(M_new, cap_loc, d->n_q_heads, max_sel_chunks,
+                                    attend_group(B, M_new, d->n_q_heads));
   return r > a ? r : a;
 }
 
@@ -526,8 +542,9 @@ int32_t msa_interleave_batch_step(const msa_dims* d, msa_interleave_batch* st,
   rc = check_attend_args(d, Q_new, M_new, st->K_loc, st->V_loc, M_loc, Kbar, Vbar, n_chunks, dco,
                          n_docs, st->topk_ids, st->n_sel, max_sel_chunks, out);
   if (rc) return rc;
+  const int32_t grp = attend_group(B, M_new, d->n_q_heads);
   const size_t need_r = route_topk_ws(B, M_new, n_chunks, n_docs, d->top_k);
-  const size_t need_a = attend_workspace(M_new, M_loc, d->n_q_heads, max_sel_chunks);
+  const size_t need_a = attend_workspace(M_new, M_loc, d->n_q_heads, max_sel_chunks, grp);
   if (ws == nullptr || ws_bytes < need_r || ws_bytes < need_a)
     return fail(MSA_ERR_WORKSPACE, "interleave_batch workspace too small");
   const void* kb = nullptr;
@@ -553,6 +570,13 @@ int32_t msa_interleave_batch_step(const msa_dims* d, msa_interleave_batch* st,
                            row * 2 * M_new, hipMemcpyDeviceToDevice, s));
     MSA_HIP(hipMemcpyAsync(vl + (size_t)st->n_loc * row, V_new + (size_t)b * M_new * row,
                            row * 2 * M_new, hipMemcpyDeviceToDevice, s));
+  }
+  // queries go through the attention launches in groups of grp (one group
+  // per set of launches when the multi-token kernel serves the shape)
+  for (int32_t b = 0; b < B; b += grp) {
+    const int32_t nb = B - b < grp ? B - b : grp;
+    msa_bf16* kl = st->K_loc + (size_t)b * st->cap_loc * row;
+    msa_bf16* vl = st->V_loc + (size_t)b * st->cap_loc * row;
     AttendArgs a;
     a.Q = Q_new + (size_t)b * M_new * q_row; a.M = M_new; a.n_q_heads = d->n_q_heads;
     a.K_loc = kl; a.V_loc = vl; a.M_loc = M_loc; a.k_loc_rotated = 0;
@@ -563,7 +587,11 @@ int32_t msa_interleave_batch_step(const msa_dims* d, msa_interleave_batch* st,
     a.max_sel_chunks = max_sel_chunks; a.pos0 = st->pos0; a.theta = (double)d->rope_theta;
     a.kv_on_host = kv_on_host ? 1 : 0;
     a.out = out + (size_t)b * M_new * q_row; a.out_f32 = nullptr;
-    rc = launch_attend(a, ws, ws_bytes, s);
+    AttendBatch ab;
+    ab.nb = nb;
+    ab.q_stride = (int64_t)M_new * q_row;
+    ab.kv_stride = (int64_t)st->cap_loc * row;
+    rc = launch_attend(a, ws, ws_bytes, s, nb > 1 ? &ab : nullptr);
     if (rc) return rc;
   }
   st->n_loc = M_loc;

@@ -571,6 +571,10 @@ struct MtArgs {
   int64_t max_sel;
   int32_t key_split;
   float* Opart; float* ML;
+  // queries of a batch: blockIdx.z = query · n_splits + split; per-query
+  // element strides of Qr, Kr, Vloc, the partials and the (m, l) pairs
+  int32_t n_splits;
+  int64_t qr_stride, kr_stride, v_stride, op_stride, ml_stride;
 };
 
 // Rotates the query rows (at pos0 + M_loc - M + u, then scaled by qscale) and,
@@ -582,32 +586,41 @@ __global__ __launch_bounds__(256) void rot_qk_kernel(const uint16_t* __restrict_
                                                      int32_t M_loc, const int32_t* __restrict__ n_sel,
                                                      int32_t top_k, int64_t pos0_arg, RopeTab rt,
                                                      float qscale, uint16_t* __restrict__ Qr,
-                                                     uint16_t* __restrict__ Kr) {
+                                                     uint16_t* __restrict__ Kr, int32_t nb,
+                                                     int64_t q_stride, int64_t kl_stride) {
+  // nb queries: query b's Q at Q + b·q_stride, its local keys at
+  // Kl + b·kl_stride, its n_sel at n_sel[b]; outputs packed per query
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nq = (int64_t)M * Hq * (kDim / 2);
   const int64_t nk = Kr ? (int64_t)M_loc * kHeads * (kDim / 2) : 0;
-  if (idx >= nq + nk) return;
-  const int64_t pos0 = pos0_arg < 0 ? (int64_t)clamp_nsel(n_sel, top_k) : pos0_arg;
+  if (idx >= (nq + nk) * nb) return;
   const uint16_t* src;
   uint16_t* dst;
   int64_t row, pos;
-  int m;
+  int m, b;
   float sc = 1.0f;
-  if (idx < nq) {
-    row = idx / (kDim / 2);
-    m = (int)(idx % (kDim / 2));
-    pos = pos0 + (M_loc - M) + row / Hq;
-    src = Q;
-    dst = Qr;
-    sc = qscale;
-  } else {
-    const int64_t j = idx - nq;
+  if (idx < nq * nb) {
+    b = (int)(idx / nq);
+    const int64_t j = idx - (int64_t)b * nq;
     row = j / (kDim / 2);
     m = (int)(j % (kDim / 2));
-    pos = pos0 + row / kHeads;
-    src = Kl;
-    dst = Kr;
+    src = Q + b * q_stride;
+    dst = Qr + (int64_t)b * M * Hq * kDim;
+    sc = qscale;
+  } else {
+    const int64_t j0 = idx - nq * nb;
+    b = (int)(j0 / nk);
+    const int64_t j = j0 - (int64_t)b * nk;
+    row = j / (kDim / 2);
+    m = (int)(j % (kDim / 2));
+    src = Kl + b * kl_stride;
+    dst = Kr + (int64_t)b * M_loc * kHeads * kDim;
   }
+  const int64_t pos0 = pos0_arg < 0 ? (int64_t)clamp_nsel(n_sel + b, top_k) : pos0_arg;
+  if (idx < nq * nb)
+    pos = pos0 + (M_loc - M) + row / Hq;
+  else
+    pos = pos0 + row / kHeads;
   const float2 cs = cis_hw((double)pos * rt.om[m]);
   const float x = bf16f(src[row * kDim + m]), y = bf16f(src[row * kDim + m + 64]);
   dst[row * kDim + m] = f2bf((x * cs.x - y * cs.y) * sc);
@@ -621,7 +634,18 @@ __device__ __forceinline__ int k_row(int q) {
 
 template <bool HOST_KV>
 __global__ __launch_bounds__(kMtThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_mt_kernel(const MtArgs a) {
+void attn_mt_kernel(const MtArgs args) {
+  // this workgroup's query of the batch: its own rows, local keys, selection
+  // and partials (uniform pointer arithmetic)
+  const int qb = blockIdx.z / args.n_splits;
+  MtArgs a = args;
+  a.Qr += qb * args.qr_stride;
+  a.Kr += qb * args.kr_stride;
+  a.Vloc += qb * args.v_stride;
+  a.sel_ids += (int64_t)qb * args.top_k;
+  a.n_sel += qb;
+  a.Opart += qb * args.op_stride;
+  a.ML += qb * args.ml_stride;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kMtBufElems];
   __shared__ int32_t s_off[kMaxSel];
   __shared__ int64_t s_start[kMaxSel];
@@ -634,7 +658,7 @@ void attn_mt_kernel(const MtArgs a) {
   const int half = lane >> 5;
   const int rg = blockIdx.x;
   const int g = blockIdx.y;
-  const int split = blockIdx.z;
+  const int split = blockIdx.z - qb * args.n_splits;
   const int G = a.Hq / kHeads;
   const int rows_g = a.M * G;
   const int64_t n_rows_tot = (int64_t)a.M * a.Hq;
@@ -889,13 +913,23 @@ void attn_mt_kernel(const MtArgs a) {
 // read first, then the partials are weighted by exp2(m_s - max) and summed in
 // split order.
 constexpr int kCombRows = 8;
-__global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restrict__ Opart,
-                                                           const float* __restrict__ ML,
+__global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restrict__ Opart_all,
+                                                           const float* __restrict__ ML_all,
                                                            int32_t n_splits, int64_t n_rows,
-                                                           uint16_t* __restrict__ out,
-                                                           float* __restrict__ out_f32) {
-  const int64_t row = (int64_t)blockIdx.x * kCombRows + (threadIdx.x >> 5);
-  if (row >= n_rows) return;
+                                                           int32_t nb, int64_t op_stride,
+                                                           int64_t ml_stride,
+                                                           uint16_t* __restrict__ out_all,
+                                                           float* __restrict__ out_f32_all) {
+  // nb queries of n_rows rows each; query b's partials at b·op_stride /
+  // b·ml_stride, its output rows after the previous queries'
+  const int64_t grow_all = (int64_t)blockIdx.x * kCombRows + (threadIdx.x >> 5);
+  if (grow_all >= n_rows * nb) return;
+  const int64_t qb = grow_all / n_rows;
+  const int64_t row = grow_all - qb * n_rows;
+  const float* Opart = Opart_all + qb * op_stride;
+  const float* ML = ML_all + qb * ml_stride;
+  uint16_t* out = out_all + qb * n_rows * kDim;
+  float* out_f32 = out_f32_all ? out_f32_all + qb * n_rows * kDim : nullptr;
   const int d = (threadIdx.x & 31) * 4;
   float mx = -INFINITY;
   for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, ML[((int64_t)s * n_rows + row) * 2]);
@@ -925,9 +959,13 @@ struct AttnPlan {
   int32_t row_blocks, key_split, n_splits;
   bool rot_inline;
   size_t off_kr, off_qr, off_opart, off_ml, total;
+  int64_t kr_q, qr_q, op_q, ml_q;   // per-query elements of each workspace part
 };
 
-AttnPlan attn_plan(int32_t M, int32_t M_loc, int32_t Hq, int64_t max_sel) {
+// The split plan is that of one query whatever nb is (so each query of a
+// batch computes exactly what it would alone); the workspace holds nb
+// queries' rotated rows and partials.
+AttnPlan attn_plan(int32_t M, int32_t M_loc, int32_t Hq, int64_t max_sel, int32_t nb = 1) {
   AttnPlan p;
   const int32_t G = Hq / kHeads;
   const int32_t rows_g = M * G;
@@ -960,11 +998,15 @@ AttnPlan attn_plan(int32_t M, int32_t M_loc, int32_t Hq, int64_t max_sel) {
   int64_t ws_splits = want < kMaxSplits ? want : kMaxSplits;
   if (ws_splits > tiles) ws_splits = tiles;
   if (ws_splits < p.n_splits) ws_splits = p.n_splits;
+  p.kr_q = (int64_t)M_loc * kHeads * kDim;
+  p.qr_q = p.multi ? (int64_t)M * Hq * kDim : 0;
+  p.op_q = ws_splits * M * Hq * kDim;
+  p.ml_q = 2 * ws_splits * M * Hq;
   size_t o = 0;
-  p.off_kr = o; o = align_up(o + 2 * (size_t)M_loc * kHeads * kDim, 256);
-  p.off_qr = o; o = align_up(o + (p.multi ? 2 * (size_t)M * Hq * kDim : 0), 256);
-  p.off_opart = o; o = align_up(o + 4 * (size_t)ws_splits * M * Hq * kDim, 256);
-  p.off_ml = o; o = align_up(o + 4 * 2 * (size_t)ws_splits * M * Hq, 256);
+  p.off_kr = o; o = align_up(o + 2 * (size_t)nb * p.kr_q, 256);
+  p.off_qr = o; o = align_up(o + 2 * (size_t)nb * p.qr_q, 256);
+  p.off_opart = o; o = align_up(o + 4 * (size_t)nb * p.op_q, 256);
+  p.off_ml = o; o = align_up(o + 4 * (size_t)nb * p.ml_q, 256);
   p.total = o;
   return p;
 }
@@ -978,13 +1020,22 @@ RopeTab rope_tab(double theta) {
 
 }  // namespace
 
-size_t attend_workspace(int32_t M, int32_t M_loc, int32_t n_q_heads, int64_t max_sel_chunks) {
-  return attn_plan(M, M_loc, n_q_heads, max_sel_chunks).total;
+size_t attend_workspace(int32_t M, int32_t M_loc, int32_t n_q_heads, int64_t max_sel_chunks,
+                        int32_t nb) {
+  return attn_plan(M, M_loc, n_q_heads, max_sel_chunks, nb).total;
 }
 
-int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
-  const AttnPlan p = attn_plan(a.M, a.M_loc, a.n_q_heads, a.max_sel_chunks);
+bool attend_is_multi(int32_t M, int32_t n_q_heads) {
+  return M * (n_q_heads / kHeads) > kRowTile;
+}
+
+int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
+                  const AttendBatch* batch) {
+  const int32_t nb = batch ? batch->nb : 1;
+  const AttnPlan p = attn_plan(a.M, a.M_loc, a.n_q_heads, a.max_sel_chunks, nb);
   if (ws_bytes < p.total) return fail(MSA_ERR_WORKSPACE, "attend workspace too small");
+  if (nb > 1 && (!p.multi || batch->q_stride != (int64_t)a.M * a.n_q_heads * kDim))
+    return fail(MSA_ERR_UNSUPPORTED, "batched attention: multi-token shapes with packed queries only");
   char* base = static_cast<char*>(ws);
   uint16_t* Kr = reinterpret_cast<uint16_t*>(base + p.off_kr);
   float* Opart = reinterpret_cast<float*>(base + p.off_opart);
@@ -995,11 +1046,13 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s)
   if (p.multi) {
     uint16_t* Qr = reinterpret_cast<uint16_t*>(base + p.off_qr);
     uint16_t* kr_dst = a.k_loc_rotated ? nullptr : Kr;
-    const int64_t pairs = ((int64_t)a.M * a.n_q_heads + (kr_dst ? (int64_t)a.M_loc * kHeads : 0)) *
-                          (kDim / 2);
+    const int64_t q_stride = batch ? batch->q_stride : 0;
+    const int64_t kl_stride = batch ? batch->kv_stride : 0;
+    const int64_t pairs =
+        ((int64_t)a.M * a.n_q_heads + (kr_dst ? (int64_t)a.M_loc * kHeads : 0)) * (kDim / 2) * nb;
     hipLaunchKernelGGL(rot_qk_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s,
                        a.Q, a.M, a.n_q_heads, a.K_loc, a.M_loc, a.n_sel, a.top_k, a.pos0, rt,
-                       qk_scale_log2, Qr, kr_dst);
+                       qk_scale_log2, Qr, kr_dst, nb, q_stride, kl_stride);
     MSA_LAUNCH_CHECK("rot_qk_kernel launch");
     MtArgs k;
     k.Qr = Qr; k.M = a.M; k.Hq = a.n_q_heads;
@@ -1010,15 +1063,22 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s)
     k.max_sel = a.max_sel_chunks;
     k.key_split = p.key_split;
     k.Opart = Opart; k.ML = ML;
-    const dim3 grid(p.row_blocks, kHeads, p.n_splits);
+    k.n_splits = p.n_splits;
+    k.qr_stride = p.qr_q;
+    k.kr_stride = a.k_loc_rotated ? kl_stride : p.kr_q;
+    k.v_stride = kl_stride;
+    k.op_stride = p.op_q;
+    k.ml_stride = p.ml_q;
+    const dim3 grid(p.row_blocks, kHeads, p.n_splits * nb);
     if (a.kv_on_host)
       hipLaunchKernelGGL(attn_mt_kernel<true>, grid, dim3(kMtThreads), 0, s, k);
     else
       hipLaunchKernelGGL(attn_mt_kernel<false>, grid, dim3(kMtThreads), 0, s, k);
     MSA_LAUNCH_CHECK("attn_mt_kernel launch");
     const int64_t n_rows = (int64_t)a.M * a.n_q_heads;
-    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)((n_rows + kCombRows - 1) / kCombRows)),
-                       dim3(256), 0, s, Opart, ML, p.n_splits, n_rows, a.out, a.out_f32);
+    hipLaunchKernelGGL(combine_rows_kernel,
+                       dim3((unsigned)((n_rows * nb + kCombRows - 1) / kCombRows)), dim3(256), 0,
+                       s, Opart, ML, p.n_splits, n_rows, nb, p.op_q, p.ml_q, a.out, a.out_f32);
     MSA_LAUNCH_CHECK("combine_rows_kernel launch");
     return MSA_OK;
   } else {
