@@ -54,9 +54,10 @@ __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w <
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// float -> bf16, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  const uint32_t u = __float_as_uint(f);
+// float -> bf16, round to nearest even; NaN stays a quiet NaN. (Host and
+// device: the host build is what the rounding tests call.)
+__host__ __device__ __forceinline__ uint16_t f2bf(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
   const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
   // NaN stays NaN (quiet bit set); selects, not branches, so callers unroll
   return (uint16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : rne);
@@ -68,15 +69,15 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 // 8 + 2, so the two steps round exactly once. The toward-zero narrowing is the
 // hardware's nearest-even conversion stepped back by one unit when it rounded
 // away from zero (a library toward-zero conversion costs several times more).
-__device__ __forceinline__ uint16_t d2bf(double x) {
+__host__ __device__ __forceinline__ uint16_t d2bf(double x) {
   const float f = (float)x;
   const double d = (double)f;
-  uint32_t u = __float_as_uint(f);
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
   if (d != x) {
     if (fabs(d) > fabs(x)) u -= 1u;
     u |= 1u;
   }
-  const uint16_t b = f2bf(__uint_as_float(u));
+  const uint16_t b = f2bf(__builtin_bit_cast(float, u));
   return (x != x) ? (uint16_t)0x7fc0u : b;
 }
 
