@@ -448,19 +448,22 @@ def test_interleave_rounds():
     assert il.n_loc == 3 * 96
 
 
-def test_interleave_batch_equals_single_queries():
-    """Three queries advanced together through three rounds give, bit for
-    bit, what three single-query states give (one batched routing scan, then
-    each query's own selection and attention); query 1 is also checked
+@pytest.mark.parametrize("B,M_new", [(3, 96), (9, 64)])
+def test_interleave_batch_equals_single_queries(B, M_new):
+    """Queries advanced together through three rounds give, bit for bit, what
+    single-query states give (one batched routing scan, then each query's own
+    selection and attention, up to 8 queries per set of attention launches:
+    nine queries take a group of 8 and a group of 1); query 1 is also checked
     against the oracle."""
-    _banner("interleave batch of 3 queries, 3 rounds")
-    mem, chains = synth.cfg5_memory("cpu", seed=11, n_tokens=120_000, n_queries=3, hops=3)
+    _banner(f"interleave batch of {B} queries, 3 rounds of {M_new}")
+    # enough documents for B chains of 3 distinct planted documents
+    mem, chains = synth.cfg5_memory("cpu", seed=11, n_tokens=40_000 * B, n_queries=B, hops=3)
+    assert all(len(c) == 3 for c in chains)
     Kb, Vb, Rb, dco_h, dco = _pool_gpu(mem)
     oK, oV, oR, odco = O.pool(u16(mem.K), u16(mem.V), u16(mem.KR), mem.doc_token_offsets)
     d = msa.dims(top_k=4)
     max_sel = int(np.diff(dco_h).max()) * 4
     n_docs = len(dco_h) - 1
-    B, M_new = 3, 96
     batch = msa.InterleaveBatch(B, n_docs, cap_loc=3 * M_new, d=d)
     singles = [msa.Interleave(n_docs, cap_loc=3 * M_new, d=d) for _ in range(B)]
     st1 = O.InterleaveState(n_docs)
@@ -603,12 +606,14 @@ def test_route_long_queries_mean(B, M):
 
 
 @pytest.mark.parametrize("n_chunks", [1, 127, 129, 3001])
-@pytest.mark.parametrize("B,M", [(1, 256), (3, 256), (2, 512), (1, 768)])
+@pytest.mark.parametrize("B,M", [(1, 256), (3, 256), (2, 512), (1, 768), (5, 256), (9, 512)])
 def test_route_tiled_scan(n_chunks, B, M):
     """Queries of whole 256-token tiles take the tiled contraction scan: one
     tile per query (the two row halves merged in the workgroup), and two or
     three tiles per query folded by the second kernel, with chunk counts that
-    fill no 128- or 256-chunk tile or end mid-tile."""
+    fill no 128- or 256-chunk tile or end mid-tile. Four or more row tiles
+    take the blocked workgroup order (5 and 18 row tiles leave its last block
+    part empty)."""
     _banner(f"route tiled n_chunks={n_chunks} B={B} M={M}")
     st = _store(n_chunks, 900 + n_chunks, lo=1, hi=7)
     QR = synth.randn_bf16((B, M, 8, 128), synth.torch_gen(14, n_chunks * 1000 + B * 300 + M))
