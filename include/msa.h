@@ -149,6 +149,12 @@ int32_t msa_encode_pool(const msa_dims* d, const msa_bf16* K, const msa_bf16* V,
  *     in rank order; entries past n_sel are -1 / -inf.
  *   n_sel [B] int32 (written).
  *   Norms are clamped at 1e-6 before dividing; a NaN score ranks last.
+ *   Precision: with at most 8 query rows in all the cosines are fp32-exact
+ *     (q̂ kept as a bf16 hi + lo pair); with more rows q̂ is rounded to bf16,
+ *     and when M is a multiple of 256 k̂ = k/‖k‖ is rounded to bf16 as well
+ *     (the head sum is then one contraction); a chunk score moves by ~1e-4 at
+ *     most. The path depends on B·M <= 8 and on M only, so a query of more
+ *     than 8 tokens gets the same scores alone or in any batch.
  *   ws / ws_bytes: at least msa_route_topk_workspace() bytes. */
 size_t msa_route_topk_workspace(const msa_dims* d, int32_t B, int32_t M, int64_t n_chunks,
                                 int32_t n_docs);
@@ -187,8 +193,9 @@ int32_t msa_route_topk_noalloc(const msa_dims* d, const msa_bf16* QR, int32_t B,
  * themselves (for instance to supervise routing) or to time the scan alone.
  * msa_route_scores: chunk_scores [B, n_chunks] fp32 (written) holds
  *   S_c = max_t (or mean_t) mean_h cos(Q^R_{t,h}, K̄^R_{c,h}) for each query.
- *   Workspace: msa_route_scores_workspace() bytes (0 when every query's tokens
- *   fit one row tile; then ws may be NULL).
+ *   Workspace: msa_route_scores_workspace() bytes: partial maxima when a
+ *   query's tokens span several row tiles, and the normalised query rows when
+ *   M is a multiple of 256; 0 otherwise, and then ws may be NULL.
  * msa_select_topk: reduces chunk_scores [B, n_chunks] to document scores
  *   (max over each document's chunks; max-merged into doc_scores when
  *   accumulate != 0) and selects the top_k documents exactly as
