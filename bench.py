@@ -19,7 +19,9 @@ value = memory tokens routed per second per query = 18 × 100M / step time.
 The JSON line also carries the roofline of the dominant kernel (the routing
 scan: 2048 algorithmic bytes per chunk, timed with HIP events around its own
 launches inside the timed region) and the CPU oracle timed on a bounded sample.
-Unless --no-sub is given, it also carries "sub_results" for the 16M batched
+Unless --no-sub is given, it also carries "sub_results": two decode queries
+pipelined on two streams over the same 100M store (one query's PCIe-bound
+gather and attention overlap the other's HBM-bound scan), and the 16M batched
 routing, the 10M pooling and the 10M interleave workloads below, each with its
 own roofline and oracle baseline.
 
@@ -309,6 +311,15 @@ def workload_100m(args):
         r["cpu_baseline"] = cpu_baseline_100m(args, store, L, queries[0], atts[0])
     else:
         r["cpu_baseline"] = None
+    if not args.no_sub:
+        # the pipelined decode on the same store: two queries on two streams
+        log(args, "sub-workload pipeline_100m (2 concurrent queries)")
+        p = pipeline_on(args, store, queries, atts, 2)
+        if r["cpu_baseline"] is not None:
+            p["cpu_baseline"] = dict(r["cpu_baseline"],
+                                     sample=r["cpu_baseline"]["sample"] + "; the oracle routes "
+                                     "one query at a time, so its rate for two is the same")
+        r["_pipeline"] = p
     return r
 
 
@@ -840,18 +851,17 @@ def workload_aux(args):
 # pipeline: concurrent decode queries over the 100M-token memory, one stream
 # per query, so one query's PCIe-bound attention overlaps another's scan
 # ---------------------------------------------------------------------------
-def workload_pipeline(args):
+def pipeline_on(args, store, queries, atts, Qn):
+    """Qn concurrent decode queries over an existing 100M store: each query's
+    layers in order on its own stream, against the same queries one after
+    another on one stream."""
     import numpy as np
     import torch
 
     import routed_sparse_attention_amd as msa
-    import synth
 
     dev = "cuda"
-    L, Qn = args.layers, args.queries
-    store, queries, atts = synth.cfg4_100m(dev, n_chunks=args.chunks, n_layers=L,
-                                           kv_pinned=(args.kv == "host"))
-    torch.cuda.synchronize()
+    L = len(queries)
     C, N = store.n_chunks, store.n_docs
     d = msa.dims()
     dco = torch.from_numpy(store.doc_chunk_offsets).to(dev)
@@ -925,11 +935,35 @@ def workload_pipeline(args):
                                  f"{tokens / 1e6:.0f}M-token memory; K̄/V̄ "
                                  f"{'in pinned host memory' if args.kv == 'host' else 'in HBM'}",
                      "queries": Qn, "layers": L, "memory_tokens": tokens})
+    # the scans of all queries over the whole step: the router keys they read
+    # against the HBM peak (the other stages overlap them)
+    scan_bytes = C * ROW_BYTES + C * 4
+    achieved = Qn * L * scan_bytes / (ms_c * 1e-3) / 1e9
     r.update({"ms_concurrent": ms_c, "ms_one_after_another": ms_s,
               "speedup": ms_s / ms_c,
               "per_query_latency_ms": ms_c,
-              "roofline": None, "cpu_baseline": None})
+              "roofline": {"bound": "hbm",
+                           "kernel": "scan_valu_kernel<1> (msa_route_scores), every query's "
+                                     "scans over the whole step",
+                           "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": achieved / HBM_PEAK_GBS,
+                           "traffic": stored_traffic("route_scan", [csrc("msa_route.hip"),
+                                                                    csrc("msa_internal.h")]),
+                           "bytes_per_launch": scan_bytes,
+                           "launches_per_step": Qn * L},
+              "cpu_baseline": None})
     return r
+
+
+def workload_pipeline(args):
+    import torch
+
+    import synth
+
+    store, queries, atts = synth.cfg4_100m("cuda", n_chunks=args.chunks, n_layers=args.layers,
+                                           kv_pinned=(args.kv == "host"))
+    torch.cuda.synchronize()
+    return pipeline_on(args, store, queries, atts, args.queries)
 
 
 def main():
@@ -950,6 +984,12 @@ def main():
         # the other measured workloads, each with its own roofline and oracle
         # baseline, carried on the same line (the 100M store is freed first)
         subs = {}
+        pipe = r.pop("_pipeline", None)
+        if pipe is not None:
+            for k in ("n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline",
+                      "dtype", "data"):
+                pipe.pop(k, None)
+            subs["pipeline_100m_2q"] = pipe
         for name, sub in (("route_16m_batched", workload_route16m), ("pool_10m", workload_pool10m),
                           ("interleave_10m", workload_interleave)):
             torch.cuda.synchronize()
