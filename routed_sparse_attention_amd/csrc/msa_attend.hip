@@ -61,6 +61,23 @@ constexpr int kRowTile = 32;
 constexpr int kMaxSplits = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Base-2 exponential of the online softmax: the hardware instruction alone.
+// Its arguments are scores minus the running row maximum (<= 0), so a result
+// below fp32's normal range (a weight under 2^-126 of the row's largest) is
+// flushed to zero instead of being scaled through the denormal range, which
+// a bf16 output cannot see.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Keys per split. The launch fixes the number of splits from the largest
+// context the call allows (max_sel chunks + the local keys); each workgroup
+// cuts the context actually selected into that many runs of whole tiles, so
+// a selection far below the capacity still spreads over every split. Every
+// workgroup of a query derives the same count from the same chunk list.
+__device__ __forceinline__ int split_keys(int n_keys, int n_splits, int tile) {
+  const int tiles = (n_keys + tile - 1) / tile;
+  return ((tiles + n_splits - 1) / n_splits) * tile;
+}
+
 // rotation frequencies omega_m = theta^(-2m/128) (host-made)
 struct RopeTab {
   double om[kDim / 2];
@@ -74,7 +91,7 @@ struct AttnArgs {
   const int64_t* dco; int32_t n_docs;
   const int32_t* sel_ids; const int32_t* n_sel; int32_t top_k;
   int64_t max_sel; int64_t pos0;
-  int32_t key_split; float qk_scale_log2;
+  float qk_scale_log2;
   float* Opart; float* ML;
   RopeTab rt;
 };
@@ -242,8 +259,9 @@ void attn_kernel(const AttnArgs a) {
     s_start[lane] = start;
   }
   const int n_keys = n_mem + a.M_loc;
-  const int k_begin = split * a.key_split;
-  const int k_end = min(k_begin + a.key_split, n_keys);
+  const int key_split = split_keys(n_keys, (int)gridDim.z, kKeyTile);
+  const int k_begin = split * key_split;
+  const int k_end = min(k_begin + key_split, n_keys);
   const int64_t pos0 = a.pos0 < 0 ? (int64_t)ns : a.pos0;
 
   // Accumulator rows held by this lane: r(v) = base_r + off(v), with
@@ -427,8 +445,8 @@ void attn_kernel(const AttnArgs a) {
       t = fmaxf(t, dpp_f<0x140>(t));   // row_mirror
       t = fmaxf(t, __shfl_xor(t, 16));
       const float mn = fmaxf(mrow[v], t);
-      const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(mrow[v] - mn);
-      p[v] = (mn == -INFINITY) ? 0.0f : exp2f(sv - mn);
+      const float alpha = (mn == -INFINITY) ? 1.0f : exp2_hw(mrow[v] - mn);
+      p[v] = (mn == -INFINITY) ? 0.0f : exp2_hw(sv - mn);
       lpart[v] = lpart[v] * alpha + p[v];
       mrow[v] = mn;
 #pragma unroll
@@ -569,7 +587,6 @@ struct MtArgs {
   const int64_t* dco; int32_t n_docs;
   const int32_t* sel_ids; const int32_t* n_sel; int32_t top_k;
   int64_t max_sel;
-  int32_t key_split;
   float* Opart; float* ML;
   // queries of a batch: blockIdx.z = query · n_splits + split; per-query
   // element strides of Qr, Kr, Vloc, the partials and the (m, l) pairs
@@ -707,12 +724,13 @@ void attn_mt_kernel(const MtArgs args) {
   // ---- keys of this split, cut where the workgroup's last token stops
   //      seeing local keys (causal)
   const int n_keys = n_mem + a.M_loc;
-  const int k_begin = split * a.key_split;
+  const int key_split = split_keys(n_keys, a.n_splits, kMtKeys);
+  const int k_begin = split * key_split;
   const int r_last = min(rows_g, (rg + 1) * kMtRows) - 1;
   const int u_first = min(rg * kMtRows, rows_g - 1) / G;
   const int lim_wg_hi = n_mem + (a.M_loc - a.M) + r_last / G;    // last key any row sees
   const int lim_wg_lo = n_mem + (a.M_loc - a.M) + u_first;       // last key every row sees
-  const int k_end = min(min(k_begin + a.key_split, n_keys), lim_wg_hi + 1);
+  const int k_end = min(min(k_begin + key_split, n_keys), lim_wg_hi + 1);
   const int n_tiles = k_end > k_begin ? (k_end - k_begin + kMtKeys - 1) / kMtKeys : 0;
   const int lim_row = n_mem + (a.M_loc - a.M) + u;               // last key this row sees
 
@@ -846,7 +864,7 @@ void attn_mt_kernel(const MtArgs args) {
     // rescale only when some row's maximum moved (the common case after the
     // first tiles is that none did)
     if (__any(m_new != m_run)) {
-      const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
+      const float alpha = live ? exp2_hw(m_run - m_new) : 1.0f;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -854,6 +872,9 @@ void attn_mt_kernel(const MtArgs args) {
         for (int v = 0; v < 16; ++v) O[db][v] *= alpha;
     }
     m_run = m_new;
+    // a row with every key so far masked has m = -inf and S = -inf: its
+    // weights are exp2(-inf - 0) = 0
+    const float m_use = live ? m_new : 0.0f;
     float psum = 0.0f;
     uint4 pb[2][2];
 #pragma unroll
@@ -863,7 +884,7 @@ void attn_mt_kernel(const MtArgs args) {
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = live ? exp2f(S[kb][8 * sg + e] - m_new) : 0.0f;
+          p[e] = exp2_hw(S[kb][8 * sg + e] - m_use);
           psum += p[e];
         }
         pb[kb][sg] = pack8(p);
@@ -1061,7 +1082,6 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
     k.dco = a.dco; k.n_docs = a.n_docs;
     k.sel_ids = a.sel_ids; k.n_sel = a.n_sel; k.top_k = a.top_k;
     k.max_sel = a.max_sel_chunks;
-    k.key_split = p.key_split;
     k.Opart = Opart; k.ML = ML;
     k.n_splits = p.n_splits;
     k.qr_stride = p.qr_q;
@@ -1090,7 +1110,6 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
     k.dco = a.dco; k.n_docs = a.n_docs;
     k.sel_ids = a.sel_ids; k.n_sel = a.n_sel; k.top_k = a.top_k;
     k.max_sel = a.max_sel_chunks; k.pos0 = a.pos0;
-    k.key_split = p.key_split;
     k.qk_scale_log2 = qk_scale_log2;
     k.Opart = Opart;
     k.ML = ML;
