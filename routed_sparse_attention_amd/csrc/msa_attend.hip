@@ -587,7 +587,7 @@ struct MtArgs {
   const int64_t* dco; int32_t n_docs;
   const int32_t* sel_ids; const int32_t* n_sel; int32_t top_k;
   int64_t max_sel;
-  float* Opart; float* ML;
+  uint16_t* Opart; float* ML;     // per split: O / l in bf16, and (m, l)
   // queries of a batch: blockIdx.z = query · n_splits + split; per-query
   // element strides of Qr, Kr, Vloc, the partials and the (m, l) pairs
   int32_t n_splits;
@@ -911,17 +911,21 @@ void attn_mt_kernel(const MtArgs args) {
     __syncthreads();
   }
 
-  // ---- this split's partial: lane (row, half) holds dims 32db + 8a + 4·half + 0..3
+  // ---- this split's partial: lane (row, half) holds dims 32db + 8a + 4·half + 0..3.
+  //      The partial is stored normalised, O / l, in bf16 (half the bytes of
+  //      fp32 for the merge to move); (m, l) stay fp32.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (row_ok) {
     const int64_t grow = (int64_t)split * n_rows_tot + (int64_t)u * a.Hq + hq;
-    float* dst = a.Opart + grow * kDim;
+    uint16_t* dst = a.Opart + grow * kDim;
+    const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(dst + db * 32 + 8 * q + 4 * half) =
-            make_float4(O[db][4 * q], O[db][4 * q + 1], O[db][4 * q + 2], O[db][4 * q + 3]);
+        *reinterpret_cast<uint2*>(dst + db * 32 + 8 * q + 4 * half) =
+            make_uint2(cvt_pk_bf16(O[db][4 * q] * inv_l, O[db][4 * q + 1] * inv_l),
+                       cvt_pk_bf16(O[db][4 * q + 2] * inv_l, O[db][4 * q + 3] * inv_l));
     if (half == 0) {
       a.ML[grow * 2] = m_run;
       a.ML[grow * 2 + 1] = l_tot;
@@ -930,11 +934,11 @@ void attn_mt_kernel(const MtArgs args) {
 }
 
 // Merges the key splits of the multi-token kernel: 32 threads per output
-// row, 4 dims each (16-byte loads of the partials); every split's (m, l) is
-// read first, then the partials are weighted by exp2(m_s - max) and summed in
-// split order.
+// row, 4 dims each (8-byte loads of the bf16 partials O_s / l_s); every
+// split's (m, l) is read first, then the partials are weighted by
+// exp2(m_s - max) · l_s and summed in split order.
 constexpr int kCombRows = 8;
-__global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restrict__ Opart_all,
+__global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t* __restrict__ Opart_all,
                                                            const float* __restrict__ ML_all,
                                                            int32_t n_splits, int64_t n_rows,
                                                            int32_t nb, int64_t op_stride,
@@ -947,7 +951,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
   if (grow_all >= n_rows * nb) return;
   const int64_t qb = grow_all / n_rows;
   const int64_t row = grow_all - qb * n_rows;
-  const float* Opart = Opart_all + qb * op_stride;
+  const uint16_t* Opart = Opart_all + qb * op_stride;
   const float* ML = ML_all + qb * ml_stride;
   uint16_t* out = out_all + qb * n_rows * kDim;
   float* out_f32 = out_f32_all ? out_f32_all + qb * n_rows * kDim : nullptr;
@@ -959,13 +963,13 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
   if (mx != -INFINITY) {
     for (int s = 0; s < n_splits; ++s) {
       const int64_t gr = (int64_t)s * n_rows + row;
-      const float w = exp2f(ML[gr * 2] - mx);
-      L += w * ML[gr * 2 + 1];
-      const float4 x = *reinterpret_cast<const float4*>(Opart + gr * kDim + d);
-      acc.x += w * x.x;
-      acc.y += w * x.y;
-      acc.z += w * x.z;
-      acc.w += w * x.w;
+      const float w = exp2f(ML[gr * 2] - mx) * ML[gr * 2 + 1];
+      L += w;
+      const uint2 x = *reinterpret_cast<const uint2*>(Opart + gr * kDim + d);
+      acc.x += w * bf16lo(x.x);
+      acc.y += w * bf16hi(x.x);
+      acc.z += w * bf16lo(x.y);
+      acc.w += w * bf16hi(x.y);
     }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -1026,7 +1030,8 @@ AttnPlan attn_plan(int32_t M, int32_t M_loc, int32_t Hq, int64_t max_sel, int32_
   size_t o = 0;
   p.off_kr = o; o = align_up(o + 2 * (size_t)nb * p.kr_q, 256);
   p.off_qr = o; o = align_up(o + 2 * (size_t)nb * p.qr_q, 256);
-  p.off_opart = o; o = align_up(o + 4 * (size_t)nb * p.op_q, 256);
+  // partials: bf16 O / l for the multi-token kernel, fp32 O otherwise
+  p.off_opart = o; o = align_up(o + (p.multi ? 2 : 4) * (size_t)nb * p.op_q, 256);
   p.off_ml = o; o = align_up(o + 4 * (size_t)nb * p.ml_q, 256);
   p.total = o;
   return p;
@@ -1082,7 +1087,7 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
     k.dco = a.dco; k.n_docs = a.n_docs;
     k.sel_ids = a.sel_ids; k.n_sel = a.n_sel; k.top_k = a.top_k;
     k.max_sel = a.max_sel_chunks;
-    k.Opart = Opart; k.ML = ML;
+    k.Opart = reinterpret_cast<uint16_t*>(base + p.off_opart); k.ML = ML;
     k.n_splits = p.n_splits;
     k.qr_stride = p.qr_q;
     k.kr_stride = a.k_loc_rotated ? kl_stride : p.kr_q;
@@ -1098,7 +1103,7 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
     const int64_t n_rows = (int64_t)a.M * a.n_q_heads;
     hipLaunchKernelGGL(combine_rows_kernel,
                        dim3((unsigned)((n_rows * nb + kCombRows - 1) / kCombRows)), dim3(256), 0,
-                       s, Opart, ML, p.n_splits, n_rows, nb, p.op_q, p.ml_q, a.out, a.out_f32);
+                       s, k.Opart, ML, p.n_splits, n_rows, nb, p.op_q, p.ml_q, a.out, a.out_f32);
     MSA_LAUNCH_CHECK("combine_rows_kernel launch");
     return MSA_OK;
   } else {
