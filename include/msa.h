@@ -37,7 +37,10 @@
  *     scratch array per GPU and its looked-up address.
  *   - Inputs are never modified, except where a call says so.
  *   - bf16 tensors are raw bit patterns (msa_bf16), row-major and contiguous:
- *     token-major raw states [T, H, 128], pooled states [C, H, 128].
+ *     token-major raw states [T, H, 128], pooled states [C, H, 128]. Each
+ *     starts at a 16-byte aligned address (kernels move them in 16-byte
+ *     vectors; hipMalloc, hipHostMalloc and torch allocations are aligned);
+ *     a misaligned one is MSA_ERR_INVALID_ARG naming the argument.
  *   - Offsets are int64 CSR: document i owns tokens [dto[i], dto[i+1]) and
  *     chunks [dco[i], dco[i+1]). Kernels clamp every index they derive from
  *     device arrays, so malformed offsets give wrong values, never an

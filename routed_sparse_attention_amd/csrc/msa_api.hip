@@ -26,6 +26,10 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+int misaligned16(const char* call, const char* name) {
+  return fail(MSA_ERR_INVALID_ARG, "%s: %s must start at a 16-byte aligned address", call, name);
+}
+
 int check_dims(const msa_dims* d) {
   if (d == nullptr) return fail(MSA_ERR_INVALID_ARG, "dims is NULL");
   if (d->head_dim != kDim)
@@ -187,6 +191,8 @@ int check_route_args(const msa_dims* d, const msa_bf16* QR, int32_t B, int32_t M
                 (long long)n_chunks);
   if (accumulate && d->token_reduce == MSA_TOKEN_REDUCE_MEAN)
     return fail(MSA_ERR_UNSUPPORTED, "route: accumulate needs the MAX token reduction");
+  MSA_A16("route", QR);
+  MSA_A16("route", KRbar);
   return MSA_OK;
 }
 
@@ -210,6 +216,12 @@ int check_attend_args(const msa_dims* d, const msa_bf16* Q, int32_t M, const msa
   if (max_sel_chunks < 0 || max_sel_chunks > ((int64_t)1 << 24))
     return fail(MSA_ERR_SHAPE, "attend: max_sel_chunks=%lld out of [0, 2^24]",
                 (long long)max_sel_chunks);
+  MSA_A16("attend", Q);
+  MSA_A16("attend", K_loc);
+  MSA_A16("attend", V_loc);
+  MSA_A16("attend", Kbar);
+  MSA_A16("attend", Vbar);
+  MSA_A16("attend", out);
   return MSA_OK;
 }
 
@@ -279,6 +291,12 @@ int32_t msa_encode_pool(const msa_dims* d, const msa_bf16* K, const msa_bf16* V,
     return fail(MSA_ERR_SHAPE, "encode_pool: n_chunks=%lld must be in [n_docs, n_tokens]",
                 (long long)n_chunks);
   if (n_chunks / 8 >= ((int64_t)1 << 31)) return fail(MSA_ERR_SHAPE, "encode_pool: too many chunks");
+  MSA_A16("encode_pool", K);
+  MSA_A16("encode_pool", V);
+  MSA_A16("encode_pool", KR);
+  MSA_A16("encode_pool", Kbar);
+  MSA_A16("encode_pool", Vbar);
+  MSA_A16("encode_pool", KRbar);
   PoolArgs a;
   a.K = K; a.V = V; a.KR = KR; a.dto = dto; a.dco = dco;
   a.n_docs = n_docs; a.n_tokens = n_tokens; a.n_chunks = n_chunks; a.chunk = d->chunk;
@@ -305,6 +323,8 @@ int32_t msa_route_scores(const msa_dims* d, const msa_bf16* QR, int32_t B, int32
   if ((int64_t)B * M > (1 << 24)) return fail(MSA_ERR_SHAPE, "route_scores: B*M too large");
   if (n_chunks < 1 || n_chunks >= ((int64_t)1 << 31))
     return fail(MSA_ERR_SHAPE, "route_scores: n_chunks=%lld out of [1, 2^31)", (long long)n_chunks);
+  MSA_A16("route_scores", QR);
+  MSA_A16("route_scores", KRbar);
   return route_scores_impl(d, QR, B, M, KRbar, n_chunks, chunk_scores, ws, ws_bytes,
                            static_cast<hipStream_t>(stream));
 }
@@ -437,6 +457,8 @@ int32_t msa_interleave_step(const msa_dims* d, msa_interleave_state* st, const m
   rc = check_route_args(d, QR_new, 1, M_new, KRbar, dco, n_docs, n_chunks, st->doc_scores, 1,
                         st->topk_ids, st->topk_scores, st->n_sel);
   if (rc) return rc;
+  MSA_A16("interleave", K_new);
+  MSA_A16("interleave", V_new);
   const int32_t M_loc = st->n_loc + M_new;
   rc = check_attend_args(d, Q_new, M_new, st->K_loc, st->V_loc, M_loc, Kbar, Vbar, n_chunks, dco,
                          n_docs, st->topk_ids, st->n_sel, max_sel_chunks, out);
@@ -535,6 +557,8 @@ int32_t msa_interleave_batch_step(const msa_dims* d, msa_interleave_batch* st,
   if (M_new < 1 || st->n_loc < 0 || (int64_t)st->n_loc + M_new > st->cap_loc)
     return fail(MSA_ERR_SHAPE, "interleave_batch: n_loc (%d) + M_new (%d) exceeds cap_loc (%d)",
                 st->n_loc, M_new, st->cap_loc);
+  MSA_A16("interleave_batch", K_new);
+  MSA_A16("interleave_batch", V_new);
   rc = check_route_args(d, QR_new, B, M_new, KRbar, dco, n_docs, n_chunks, st->doc_scores, 1,
                         st->topk_ids, st->topk_scores, st->n_sel);
   if (rc) return rc;

@@ -478,6 +478,8 @@ int32_t msa_route_aux_loss(const msa_dims* d, const msa_bf16* QR, int32_t B, int
     return fail(MSA_ERR_SHAPE, "aux_loss: B=%d M=%d out of range", B, M);
   if (max_pos < 1 || max_pos > kAuxMaxPos)
     return fail(MSA_ERR_SHAPE, "aux_loss: max_pos=%d must be in [1, %d]", max_pos, kAuxMaxPos);
+  MSA_A16("aux_loss", QR);
+  MSA_A16("aux_loss", KRbar);
   if (n_docs < 1 || n_chunks < n_docs || n_chunks >= ((int64_t)1 << 31))
     return fail(MSA_ERR_SHAPE, "aux_loss: n_docs=%d, n_chunks=%lld out of range", n_docs,
                 (long long)n_chunks);

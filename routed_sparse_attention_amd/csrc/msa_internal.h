@@ -25,6 +25,20 @@ int resolve_kv(const void* p, int on_host, const void** out, const char* name);
 // Same, with the memory kind read from the pointer.
 int resolve_any(const void* p, const void** out, const char* name);
 
+// Every bf16 tensor is read and written with 16-byte vector accesses, so
+// its base address must be a multiple of 16 (NULL passes; row strides are
+// multiples of 16 bytes by construction). Returns MSA_ERR_INVALID_ARG
+// naming the argument otherwise.
+int misaligned16(const char* call, const char* name);
+inline int check_a16(const char* call, const char* name, const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15) ? misaligned16(call, name) : 0;
+}
+#define MSA_A16(call, p)                                          \
+  do {                                                            \
+    int rc_ = ::msa::check_a16((call), #p, (p));                  \
+    if (rc_) return rc_;                                          \
+  } while (0)
+
 #define MSA_HIP(expr)                                   \
   do {                                                  \
     hipError_t e_ = (expr);                             \

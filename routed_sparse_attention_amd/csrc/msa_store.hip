@@ -135,6 +135,12 @@ int32_t msa_store_append(const msa_dims* d, msa_store* st, const msa_bf16* K, co
     return fail(MSA_ERR_INVALID_ARG, "store_append: the store keeps a tensor whose raw input "
                 "is NULL");
   if (!dto || !dto_h) return fail(MSA_ERR_INVALID_ARG, "store_append: NULL token offsets");
+  MSA_A16("store_append", K);
+  MSA_A16("store_append", V);
+  MSA_A16("store_append", KR);
+  MSA_A16("store_append", st->Kbar);
+  MSA_A16("store_append", st->Vbar);
+  MSA_A16("store_append", st->KRbar);
   if (n_new < 1) return fail(MSA_ERR_SHAPE, "store_append: n_new=%d must be >= 1", n_new);
   if (dto_h[0] != 0 || dto_h[n_new] != n_new_tokens)
     return fail(MSA_ERR_SHAPE, "store_append: token offsets must run from 0 to n_new_tokens=%lld",

@@ -218,3 +218,32 @@ def test_interleave_batch_rejects_bad_states_before_the_gpu():
     one = L.msa_interleave_step_workspace(ctypes.byref(d), 8, 64, 100, 10, 64)
     two = L.msa_interleave_batch_step_workspace(ctypes.byref(d), 2, 8, 64, 100, 10, 64)
     assert two >= one > 0
+
+
+def test_misaligned_bf16_tensors_are_rejected_before_the_gpu():
+    """Kernels move bf16 tensors in 16-byte vectors, so each must start at a
+    16-byte aligned address: a misaligned one fails with MSA_ERR_INVALID_ARG
+    naming the argument, before any device work (aligned fake addresses pass
+    these checks and fail later, on the workspace check)."""
+    L = msa.lib()
+    d = msa.dims()
+    p = ctypes.c_void_p(256)
+    bad = ctypes.c_void_p(258)
+
+    def scores(qr, kr):
+        return L.msa_route_scores(ctypes.byref(d), qr, 2, 1, kr, 100, p, None, 0, None)
+
+    assert scores(bad, p) == -1 and b"QR must start at a 16-byte" in L.msa_last_error()
+    assert scores(p, bad) == -1 and b"KRbar" in L.msa_last_error()
+    assert _route(d, ptr=258) == -1 and b"route: QR" in L.msa_last_error()
+
+    def attend(q=p, kl=p, vl=p, kb=p, vb=p, out=p):
+        return L.msa_sparse_attend(ctypes.byref(d), q, 4, kl, vl, 8, 0, kb, vb, 0, 8, p, 2, p, p,
+                                   8, -1, out, None, p, 0, None)
+
+    assert attend() == -3                           # aligned: reaches the workspace check
+    for name in ("q", "kl", "vl", "kb", "vb", "out"):
+        assert attend(**{name: bad}) == -1, name
+    assert b"attend: V_loc" in (attend(vl=bad), L.msa_last_error())[1]
+    rc = L.msa_encode_pool(ctypes.byref(d), p, bad, p, p, p, 1, 64, 1, p, p, p, None, 0, None)
+    assert rc == -1 and b"encode_pool: V must" in L.msa_last_error()
