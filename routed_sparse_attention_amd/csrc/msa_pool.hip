@@ -142,8 +142,9 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a, int32_t first_ten
     // Branch-free loads: token indices past the chunk's end are clamped to
     // its last token (always in bounds) and their values masked out. Two
     // register sets take turns: a group of kUnroll tokens is summed while the
-    // next group's loads are in flight.
-    const uint4* row = src4 + t0 * kRowVec;
+    // next group's loads are in flight. An empty chunk (malformed offsets can
+    // place it at t0 = n_tokens) reads the last token instead, masked out.
+    const uint4* row = src4 + min(t0, a.n_tokens - 1) * kRowVec;
     const int last = n > 0 ? n - 1 : 0;
     auto load = [&](int t, uint4* x0, uint4* x1) {
 #pragma unroll

@@ -63,6 +63,27 @@ def test_pool_ragged(mode):
         assert np.array_equal(u16(Rb[int(dco_h[doc]) + c]), u16(uvec))
 
 
+def test_pool_malformed_offsets_stay_in_bounds():
+    """Chunk offsets that give the last document two chunks past its tokens:
+    those chunks start at n_tokens, hold no token and pool to zero (their
+    loads are clamped to the last token and masked), and the well-formed
+    chunks are unchanged."""
+    _banner("pool malformed offsets: empty chunks at n_tokens")
+    mem = synth.raw_memory([65, 64], 13, "cpu")
+    d = msa.dims()
+    dco_ok = msa.plan_chunks(mem.doc_token_offsets)
+    assert dco_ok.tolist() == [0, 2, 3]
+    dco_bad = np.array([0, 2, 5], dtype=np.int64)
+    dto = torch.from_numpy(mem.doc_token_offsets).to(DEV)
+    K, V, KR = mem.K.to(DEV), mem.V.to(DEV), mem.KR.to(DEV)
+    got = msa.encode_pool(K, V, KR, dto, torch.from_numpy(dco_bad).to(DEV), 5, d)
+    ref = msa.encode_pool(K, V, KR, dto, torch.from_numpy(dco_ok).to(DEV), 3, d)
+    torch.cuda.synchronize()
+    for g, r in zip(got, ref):
+        assert torch.equal(g[:3], r)
+        assert not bool(g[3:].float().abs().max())
+
+
 def test_pool_chunk_size_and_long_doc():
     _banner("pool chunk=16 long doc")
     lengths = [5000, 3, 17]
