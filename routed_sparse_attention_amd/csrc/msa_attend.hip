@@ -1003,9 +1003,11 @@ AttnPlan attn_plan(int32_t M, int32_t M_loc, int32_t Hq, int64_t max_sel, int32_
   p.rot_inline = !p.multi && p.row_blocks == 1;
   const int64_t max_keys = max_sel + M_loc;
   // one-wave kernel: aim for >= 2048 waves (8 per CU: one tile's loads of
-  // each in flight while the others compute); multi-token kernel: about two
-  // four-wave workgroups per CU. At most kMaxSplits splits either way.
-  const int64_t target = p.multi ? 512 : 2048;
+  // each in flight while the others compute); multi-token kernel: about one
+  // four-wave workgroup per CU (256 tokens: 4 splits; 2 per CU measured
+  // slower, more split partials for no more overlap). At most kMaxSplits
+  // splits either way.
+  const int64_t target = p.multi ? 256 : 2048;
   int64_t want = target / ((int64_t)p.row_blocks * kHeads);
   if (want < 1) want = 1;
   const int64_t tiles = (max_keys + tile_keys - 1) / tile_keys;
