@@ -621,7 +621,8 @@ def workload_interleave(args):
     att_bytes = keys * 8 * 128 * 2 * 2 + 256 * 32 * 128 * 2 * 2
     att_flops = 4.0 * 256 * 32 * 128 * keys
     scan_b_bytes = C * ROW_BYTES + n_q * C * 4
-    roof_scan = roofline_of("qhat_rows_kernel + scan_gemm_kernel (msa_route_scores, "
+    roof_scan = roofline_of("qhat_rows_kernel + khat_rows_kernel + scan_gemm_dma_kernel "
+                            "(msa_route_scores, "
                             f"{n_q} queries × 256 tokens)", scan_b_us, scan_b_bytes,
                             n_q * scan_flops,
                             stored_traffic("interleave_scan", [csrc("msa_route_gemm.hip"),

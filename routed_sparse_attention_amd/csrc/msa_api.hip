@@ -115,7 +115,7 @@ ScanPlan scan_plan(int32_t B, int32_t M, int64_t C) {
     p.kind = kScanGemm;
     p.g = route_geom(B, M, M);                 // B, M; parts set below
     p.g.parts = scan_gemm_parts(M);
-    p.qhat_bytes = scan_gemm_qhat_bytes(B, M);
+    p.qhat_bytes = scan_gemm_ws_bytes(B, M, C);
   } else {
     p.kind = (int64_t)B * M > kValuTileRows ? kScanMfma : kScanValu;
     p.g = route_geom(B, M, p.kind == kScanMfma ? kMfmaTileRows : kValuTileRows);

@@ -258,13 +258,14 @@ int launch_scan_mfma(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRb
 int launch_parts_combine(const float* P, const RouteGeom& g, int64_t n_chunks,
                          int32_t token_reduce, float* S, hipStream_t s);
 // Tiled contraction scan (msa_route_gemm.hip) for M a multiple of 256: writes
-// final scores (parts == 1) or P[parts][B][C]; qhat is scan_gemm_qhat_bytes of
-// workspace for the normalised query rows.
+// final scores (parts == 1) or P[parts][B][C]; ws is scan_gemm_ws_bytes of
+// workspace (the normalised query rows, and with many row tiles the
+// normalised keys).
 bool scan_gemm_fits(int32_t M);
 int32_t scan_gemm_parts(int32_t M);
-size_t scan_gemm_qhat_bytes(int32_t B, int32_t M);
+size_t scan_gemm_ws_bytes(int32_t B, int32_t M, int64_t n_chunks);
 int launch_scan_gemm(const uint16_t* QR, int32_t B, int32_t M, const uint16_t* KRbar,
-                     int64_t n_chunks, int32_t token_reduce, float* out, uint16_t* qhat,
+                     int64_t n_chunks, int32_t token_reduce, float* out, void* ws,
                      hipStream_t s);
 
 // Doc reduce + top-k.

@@ -30,6 +30,10 @@
 //     then one exchange between the two lane halves) and the workgroup's two
 //     row halves are merged through LDS, so a 256-token query needs no second
 //     pass (longer queries write one partial per 256 rows);
+//   - with 4 or more row tiles (and 256-chunk tiles) the staged form below
+//     takes over: k̂ written once per call, q̂ and k̂ rows moved by DMA into
+//     two 64-dim LDS stages, one in flight while the other is multiplied
+//     (bit-identical scores: the same products in the same order);
 //   - workgroup order is XCD-aware (consecutive workgroups go to the 8 XCDs in
 //     turn). With 4 or more row tiles, each XCD runs blocks of 4 row tiles ×
 //     8 chunk tiles, 32 workgroups at a time, and its next block keeps the
@@ -275,6 +279,241 @@ __global__ __launch_bounds__(kGThreads) void scan_gemm_kernel(const uint16_t* __
   }
 }
 
+// ---------------------------------------------------------------------------
+// Staged form for many row tiles. k̂ is written once per call by
+// khat_rows_kernel (the same arithmetic as the staging threads' normalise
+// above, so a key's k̂ is bit-identical), and the contraction then reads q̂
+// and k̂ rows by DMA (global_load_lds, 1 KiB per instruction) into two LDS
+// stage buffers of 64 dims each: stage s + 1 is in flight while stage s is
+// multiplied, with no register staging and no normalisation in the loop.
+// The k-steps run over the same dims in the same order as the kernel above,
+// so the scores are bit-identical to it.
+//
+// Stage layout (per buffer): q̂ rows 0..255 then key rows 0..kCols-1, 128
+// bytes (8 pieces of 16 bytes) each, in blocks of 8 rows per KiB; piece p of
+// row r sits at slot 8·(r % 8) + (p ^ ((r >> 1) & 7)) of its block, so the
+// MFMA fragment reads (32 rows × one piece) hit 16 different bank groups
+// per 16 lanes. Each wave fills 8 of the blocks.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void khat_rows_kernel(const uint4* __restrict__ KR,
+                                                         int64_t n_rows,
+                                                         uint4* __restrict__ Kh) {
+  // thread (row, p): piece p of (chunk, head) row `row`; a row is one DPP row
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = t >> 4;
+  const int p = (int)(t & 15);
+  const bool ok = row < n_rows;
+  u32x4_t w = {0u, 0u, 0u, 0u};
+  if (ok) w = reinterpret_cast<const u32x4_t*>(KR)[row * 16 + p];
+  float nk = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) nk = dot2(w[j], w[j], nk);
+  const float inv = __builtin_amdgcn_rsqf(fmaxf(row_sum16(nk), kNormEps * kNormEps));
+  u32x4_t o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = cvt_pk_bf16(bf16lo(w[j]) * inv, bf16hi(w[j]) * inv);
+  if (ok) reinterpret_cast<u32x4_t*>(Kh)[row * 16 + p] = o;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gmem_void_t;
+constexpr int kSDims = 64;                          // dims per stage
+constexpr int kSRowBytes = kSDims * 2;              // 128 B per row per stage
+constexpr int kStages = kHeads * kDim / kSDims;     // 16
+// s_waitcnt: vmcnt(N) only / lgkmcnt(0) only (gfx9 field layout)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+// Workgroup barrier that keeps memory accesses on their side of it in the
+// compiler (the barrier intrinsic alone orders none). Not a memory-model
+// fence: a release fence would also wait for this wave's stage loads in
+// flight (they count as LDS writes); the explicit vmcnt / lgkmcnt waits
+// around each barrier give the ordering the hardware needs.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int kCols>
+__global__ __launch_bounds__(kGThreads) void scan_gemm_dma_kernel(const uint16_t* __restrict__ Qh,
+                                                                  GemmGeom g,
+                                                                  const uint16_t* __restrict__ Kh,
+                                                                  int64_t n_chunks,
+                                                                  int32_t token_reduce,
+                                                                  float* __restrict__ out) {
+  constexpr int kNcb = kCols / 128;                 // 32-chunk column blocks per wave
+  constexpr int kBlocks = (kGRows + kCols) / 8;     // 1 KiB blocks per stage
+  constexpr int kBlocksPerWave = kBlocks / kGWaves;
+  constexpr int kBufBytes = kBlocks * 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t buf0[kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t buf1[kBufBytes];
+
+  const int L = blockIdx.x;
+  const int Y = g.n_row_tiles;
+  const int xcd = L & 7, slot = L >> 3;
+  int x, y;
+  if (Y >= 4) {
+    const int blk = (slot >> 5) * 8 + xcd;
+    const int j = slot & 31;
+    const int RB = (Y + 3) / 4;
+    y = 4 * (blk % RB) + (j >> 3);
+    x = 8 * (blk / RB) + (j & 7);
+    if (y >= Y) return;
+  } else {
+    x = xcd + 8 * (slot / Y);
+    y = slot % Y;
+  }
+  if (x >= g.n_col_tiles) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int wr = wave & 1;
+  const int wc = wave >> 1;
+  const int64_t c_base = (int64_t)x * kCols;
+  const int64_t row_base = (int64_t)y * kGRows;
+
+  // this lane's source row and piece in each of its wave's blocks (the
+  // same for every stage; the stage adds 64 dims)
+  const uint16_t* src[kBlocksPerWave];
+#pragma unroll
+  for (int bi = 0; bi < kBlocksPerWave; ++bi) {
+    const int blk = wave * kBlocksPerWave + bi;
+    const int slot_l = lane;                     // LDS slot of this lane in the block
+    const int rl = slot_l >> 3;                  // row within the block
+    if (blk < kGRows / 8) {
+      const int r = 8 * blk + rl;
+      const int p = (slot_l & 7) ^ ((r >> 1) & 7);
+      src[bi] = Qh + (row_base + r) * kRowElems + 8 * p;
+    } else {
+      const int r = 8 * (blk - kGRows / 8) + rl;
+      const int p = (slot_l & 7) ^ ((r >> 1) & 7);
+      int64_t c = c_base + r;
+      c = c < n_chunks ? c : n_chunks - 1;       // in bounds; not stored
+      src[bi] = Kh + c * kRowElems + 8 * p;
+    }
+  }
+  auto issue = [&](int st, uint8_t* buf) {
+#pragma unroll
+    for (int bi = 0; bi < kBlocksPerWave; ++bi)
+      __builtin_amdgcn_global_load_lds((gmem_void_t*)(src[bi] + st * kSDims),
+                                       (lds_void_t*)(buf + (wave * kBlocksPerWave + bi) * 1024),
+                                       16, 0, 0);
+  };
+
+  f32x16_t acc[4][kNcb];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
+
+  // fragment byte offsets within a stage buffer (k-step ks adds pieces 2ks)
+  int a_off[4], b_off[kNcb];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int R = 128 * wr + 32 * rb + col;
+    a_off[rb] = 1024 * (R >> 3) + 16 * (8 * (R & 7));
+  }
+#pragma unroll
+  for (int cb = 0; cb < kNcb; ++cb) {
+    const int R = (kCols / 4) * wc + 32 * cb + col;
+    b_off[cb] = kGRows * kSRowBytes + 1024 * (R >> 3) + 16 * (8 * (R & 7));
+  }
+  int a_sw[4], b_sw[kNcb];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) a_sw[rb] = ((128 * wr + 32 * rb + col) >> 1) & 7;
+#pragma unroll
+  for (int cb = 0; cb < kNcb; ++cb) b_sw[cb] = (((kCols / 4) * wc + 32 * cb + col) >> 1) & 7;
+  // (a macro, not a lambda: the reads must name buf0 / buf1 themselves, so
+  // the compiler waits only for the DMA of the buffer being read)
+#define MSA_GEMM_STAGE(BUF)                                                              \
+  _Pragma("unroll") for (int ks = 0; ks < kSDims / 16; ++ks) {                             \
+    const int P = 2 * ks + half;                                                           \
+    u32x4_t a[4], b[kNcb];                                                                 \
+    _Pragma("unroll") for (int rb = 0; rb < 4; ++rb)                                       \
+      a[rb] = *reinterpret_cast<const u32x4_t*>(&BUF[a_off[rb] + 16 * (P ^ a_sw[rb])]);    \
+    _Pragma("unroll") for (int cb = 0; cb < kNcb; ++cb)                                    \
+      b[cb] = *reinterpret_cast<const u32x4_t*>(&BUF[b_off[cb] + 16 * (P ^ b_sw[cb])]);    \
+    _Pragma("unroll") for (int rb = 0; rb < 4; ++rb)                                       \
+      _Pragma("unroll") for (int cb = 0; cb < kNcb; ++cb)                                  \
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                             \
+            as_bf16x8(a[rb]), as_bf16x8(b[cb]), acc[rb][cb], 0, 0, 0);                     \
+  }
+
+  issue(0, buf0);
+  issue(1, buf1);
+  // whole ring turns with no branch inside: stages st (buf0) and st + 1
+  // (buf1), refilling each buffer with the stage two ahead once read
+  for (int st = 0; st + 2 < kStages; st += 2) {
+    wait_vm<kBlocksPerWave>();          // stage st landed (st + 1 may be in flight)
+    lds_barrier();
+    MSA_GEMM_STAGE(buf0)
+    wait_lgkm0();
+    lds_barrier();       // every wave is done reading buf0
+    issue(st + 2, buf0);
+    wait_vm<kBlocksPerWave>();          // stage st + 1 landed
+    lds_barrier();
+    MSA_GEMM_STAGE(buf1)
+    wait_lgkm0();
+    lds_barrier();
+    issue(st + 3, buf1);
+  }
+  // the last two stages
+  wait_vm<kBlocksPerWave>();
+  lds_barrier();
+  MSA_GEMM_STAGE(buf0)
+  wait_vm<0>();
+  lds_barrier();
+  MSA_GEMM_STAGE(buf1)
+  wait_lgkm0();
+  lds_barrier();
+
+#undef MSA_GEMM_STAGE
+
+  // ---- epilogue: as in scan_gemm_kernel
+  const bool mean = token_reduce == MSA_TOKEN_REDUCE_MEAN;
+  float red[kNcb];
+#pragma unroll
+  for (int cb = 0; cb < kNcb; ++cb) {
+    float r = acc[0][cb][0];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        if (rb == 0 && v == 0) continue;
+        const float t = acc[rb][cb][v];
+        r = mean ? r + t : nan_max(r, t);
+      }
+    const float o = __shfl_xor(r, 32);
+    red[cb] = mean ? (half == 0 ? r + o : o + r) : (half == 0 ? nan_max(r, o) : nan_max(o, r));
+  }
+  const float fin = (mean && g.parts == 1) ? 0.125f / (float)g.M : 0.125f;
+  float* xch = reinterpret_cast<float*>(buf0);
+  if (wr == 1 && half == 0) {
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb) xch[(wc * kNcb + cb) * 32 + col] = red[cb];
+  }
+  __syncthreads();
+  if (wr == 0 && half == 0) {
+    const int64_t b = y / g.parts, part = y % g.parts;
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb) {
+      const int64_t c = c_base + wc * (kCols / 4) + cb * 32 + col;
+      const float o = xch[(wc * kNcb + cb) * 32 + col];
+      if (c < n_chunks) out[(part * g.B + b) * n_chunks + c] = (mean ? red[cb] + o : nan_max(red[cb], o)) * fin;
+    }
+  }
+}
+
 template <int kCols>
 constexpr size_t gemm_lds_bytes() {
   return (size_t)(kGRows + kCols) * kGPitch * 2;
@@ -286,13 +525,24 @@ bool scan_gemm_fits(int32_t M) { return M >= kGRows && M % kGRows == 0; }
 
 int32_t scan_gemm_parts(int32_t M) { return M / kGRows; }
 
-size_t scan_gemm_qhat_bytes(int32_t B, int32_t M) {
-  return align_up((size_t)B * M * kHeads * kDim * 2, 256);
+// The staged form is used from kKhatMinTiles row tiles on: its k̂ pass
+// (a read and a write of the key store) then costs a few percent of the
+// contraction, while for one or two 256-row tiles it would cost as much.
+constexpr int32_t kKhatMinTiles = 4;
+static bool gemm_staged(int32_t B, int32_t M) {
+  return (int64_t)B * M / kGRows >= kKhatMinTiles;
+}
+
+size_t scan_gemm_ws_bytes(int32_t B, int32_t M, int64_t n_chunks) {
+  size_t b = align_up((size_t)B * M * kHeads * kDim * 2, 256);
+  if (gemm_staged(B, M)) b += align_up((size_t)n_chunks * kRowElems * 2, 256);
+  return b;
 }
 
 int launch_scan_gemm(const uint16_t* QR, int32_t B, int32_t M, const uint16_t* KRbar,
-                     int64_t n_chunks, int32_t token_reduce, float* out, uint16_t* qhat,
+                     int64_t n_chunks, int32_t token_reduce, float* out, void* ws,
                      hipStream_t s) {
+  uint16_t* qhat = static_cast<uint16_t*>(ws);
   if (n_chunks == 0 || B == 0) return MSA_OK;
   if (!scan_gemm_fits(M)) return fail(MSA_ERR_UNSUPPORTED, "tiled scan needs M a multiple of 256");
   GemmGeom g;
@@ -318,6 +568,17 @@ int launch_scan_gemm(const uint16_t* QR, int32_t B, int32_t M, const uint16_t* K
   }
   if (n_wg > 0x7fffffffLL) return fail(MSA_ERR_SHAPE, "tiled scan: grid too large");
   const uint4* kr = reinterpret_cast<const uint4*>(KRbar);
+  if (gemm_staged(B, M) && wide) {
+    uint16_t* khat = qhat + align_up((size_t)g.n_rows * kHeads * kDim * 2, 256) / 2;
+    const int64_t krows = n_chunks * kHeads;
+    hipLaunchKernelGGL(khat_rows_kernel, dim3((unsigned)((krows * 16 + 255) / 256)), dim3(256), 0,
+                       s, kr, krows, reinterpret_cast<uint4*>(khat));
+    MSA_LAUNCH_CHECK("khat_rows_kernel launch");
+    hipLaunchKernelGGL(scan_gemm_dma_kernel<256>, dim3((unsigned)n_wg), dim3(kGThreads), 0, s,
+                       qhat, g, khat, n_chunks, token_reduce, out);
+    MSA_LAUNCH_CHECK("scan_gemm_dma_kernel launch");
+    return MSA_OK;
+  }
   if (wide) {
     MSA_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(scan_gemm_kernel<256>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize,
