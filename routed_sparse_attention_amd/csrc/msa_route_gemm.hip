@@ -59,6 +59,47 @@ constexpr int kGPitch = 136;         // bf16 per LDS row (128 + 8: conflict-free
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
+
+// Reduces each chunk column's 128 rows of a wave tile: this lane's 64
+// accumulator values of the column (row blocks 0..3 × 16, in that order),
+// then the other lane half's through one exchange. A sum for the mean
+// reduction; for the max, a maximum that is NaN when any value is. The max
+// takes fmaxf (which skips NaN) and carries a NaN through a running sum of
+// the same values: the values are finite or NaN (head sums of products of
+// unit vectors, |value| <= 8 up to rounding), so that sum is NaN exactly when
+// one of them is. Both branches are straight-line code (the branch is
+// uniform), so the epilogue costs one or two VALU operations per value.
+template <int kNcb>
+__device__ __forceinline__ void reduce_columns(const f32x16_t (&acc)[4][kNcb], bool mean,
+                                               int half, float (&red)[kNcb]) {
+  if (mean) {
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb) {
+      float r = acc[0][cb][0];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int v = (rb == 0 ? 1 : 0); v < 16; ++v) r += acc[rb][cb][v];
+      const float o = __shfl_xor(r, 32);
+      red[cb] = half == 0 ? r + o : o + r;
+    }
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb) {
+      float r = acc[0][cb][0], z = r;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int v = (rb == 0 ? 1 : 0); v < 16; ++v) {
+          r = fmaxf(r, acc[rb][cb][v]);
+          z += acc[rb][cb][v];
+        }
+      r = z != z ? z : r;
+      const float o = __shfl_xor(r, 32);
+      red[cb] = half == 0 ? nan_max(r, o) : nan_max(o, r);
+    }
+  }
+}
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -245,20 +286,7 @@ __global__ __launch_bounds__(kGThreads) void scan_gemm_kernel(const uint16_t* __
   // ---- epilogue: reduce this wave's 128 rows per chunk column
   const bool mean = token_reduce == MSA_TOKEN_REDUCE_MEAN;
   float red[kNcb];
-#pragma unroll
-  for (int cb = 0; cb < kNcb; ++cb) {
-    float r = acc[0][cb][0];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        if (rb == 0 && v == 0) continue;
-        const float t = acc[rb][cb][v];
-        r = mean ? r + t : nan_max(r, t);
-      }
-    const float o = __shfl_xor(r, 32);
-    red[cb] = mean ? (half == 0 ? r + o : o + r) : (half == 0 ? nan_max(r, o) : nan_max(o, r));
-  }
+  reduce_columns<kNcb>(acc, mean, half, red);
   // the two row halves are one query: half 1 hands its values to half 0,
   // which writes the tile's part (query y / parts, part y % parts)
   const float fin = (mean && g.parts == 1) ? 0.125f / (float)g.M : 0.125f;   // with the head mean
@@ -482,20 +510,7 @@ __global__ __launch_bounds__(kGThreads) void scan_gemm_dma_kernel(const uint16_t
   // ---- epilogue: as in scan_gemm_kernel
   const bool mean = token_reduce == MSA_TOKEN_REDUCE_MEAN;
   float red[kNcb];
-#pragma unroll
-  for (int cb = 0; cb < kNcb; ++cb) {
-    float r = acc[0][cb][0];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        if (rb == 0 && v == 0) continue;
-        const float t = acc[rb][cb][v];
-        r = mean ? r + t : nan_max(r, t);
-      }
-    const float o = __shfl_xor(r, 32);
-    red[cb] = mean ? (half == 0 ? r + o : o + r) : (half == 0 ? nan_max(r, o) : nan_max(o, r));
-  }
+  reduce_columns<kNcb>(acc, mean, half, red);
   const float fin = (mean && g.parts == 1) ? 0.125f / (float)g.M : 0.125f;
   float* xch = reinterpret_cast<float*>(buf0);
   if (wr == 1 && half == 0) {

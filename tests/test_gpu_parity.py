@@ -673,6 +673,38 @@ def test_route_tiled_scan_staged(token_reduce):
         assert_scores_close(got[b][idx], ref, f"query {b} sampled chunk scores")
 
 
+@pytest.mark.parametrize("token_reduce", [O.TOKEN_REDUCE_MAX, O.TOKEN_REDUCE_MEAN])
+def test_route_tiled_scan_nan(token_reduce):
+    """NaN propagation on both tiled forms (staged: 2 queries × 512 rows over
+    32,845 chunks; register-staged: each query alone). A NaN in one key
+    element makes that chunk's score NaN for every query; a NaN in one query
+    row makes every score of that query NaN (max or mean over its rows).
+    Every other score equals the NaN-free run's bit for bit."""
+    B, M, C = 2, 512, 32_768 + 77
+    _banner(f"route tiled scan NaN B={B} M={M} C={C} reduce={token_reduce}")
+    st = _store(C, 43, lo=2, hi=60)
+    d = msa.dims(token_reduce=token_reduce)
+    QR = synth.randn_bf16((B, M, 8, 128), synth.torch_gen(18, 1 + token_reduce))
+    KR = st.KRbar.clone()
+    clean = msa.route_scores(QR.to(DEV), KR.to(DEV), d).cpu()
+    nan_cols = [5, 300, C - 3]
+    for c in nan_cols:
+        KR[c, c % 8, (7 * c) % 128] = float("nan")
+    QRn = QR.clone()
+    QRn[1, 300, 2, 17] = float("nan")
+    KRd = KR.to(DEV)
+    runs = [msa.route_scores(QRn.to(DEV), KRd, d).cpu()]
+    runs.append(torch.cat([msa.route_scores(QRn[b:b + 1].to(DEV), KRd, d).cpu() for b in range(B)]))
+    torch.cuda.synchronize()
+    keep = np.ones(C, dtype=bool)
+    keep[nan_cols] = False
+    for S in runs:
+        s = S.numpy()
+        assert np.isnan(s[1]).all()
+        assert np.isnan(s[0][nan_cols]).all()
+        assert torch.equal(S[0][torch.from_numpy(keep)], clean[0][torch.from_numpy(keep)])
+
+
 @pytest.mark.parametrize("B,M", [(2, 256), (3, 512)])
 def test_route_tiled_scan_mean(B, M):
     _banner(f"route tiled MEAN B={B} M={M}")
