@@ -154,7 +154,7 @@ int32_t msa_encode_pool(const msa_dims* d, const msa_bf16* K, const msa_bf16* V,
  *   Norms are clamped at 1e-6 before dividing; a NaN score ranks last.
  *   Precision: with at most 8 query rows in all the cosines are fp32-exact
  *     (q̂ kept as a bf16 hi + lo pair); with more rows q̂ is rounded to bf16,
- *     and when M is a multiple of 256 k̂ = k/‖k‖ is rounded to bf16 as well
+ *     and when M is a multiple of 128 k̂ = k/‖k‖ is rounded to bf16 as well
  *     (the head sum is then one contraction); a chunk score moves by ~1e-4 at
  *     most. The path depends on B·M <= 8 and on M only, so a query of more
  *     than 8 tokens gets the same scores alone or in any batch (with 1024 or
@@ -201,8 +201,9 @@ int32_t msa_route_topk_noalloc(const msa_dims* d, const msa_bf16* QR, int32_t B,
  *   S_c = max_t (or mean_t) mean_h cos(Q^R_{t,h}, K̄^R_{c,h}) for each query.
  *   Workspace: msa_route_scores_workspace() bytes: partial maxima when a
  *   query's tokens span several row tiles, and the normalised query rows when
- *   M is a multiple of 256 (with B·M >= 1024 also the normalised keys,
- *   n_chunks × 2 KiB); 0 otherwise, and then ws may be NULL.
+ *   M is a multiple of 128 (when M is a multiple of 256 and B·M >= 1024 also
+ *   the normalised keys, n_chunks × 2 KiB); 0 otherwise, and then ws may be
+ *   NULL.
  * msa_select_topk: reduces chunk_scores [B, n_chunks] to document scores
  *   (max over each document's chunks; max-merged into doc_scores when
  *   accumulate != 0) and selects the top_k documents exactly as

@@ -95,7 +95,7 @@ int resolve_any(const void* p, const void** out, const char* name) {
 namespace {
 
 // Scan plan: kernel choice and the workspace it needs. Queries whose token
-// count M is a multiple of 256 take the tiled contraction (msa_route_gemm.hip;
+// count M is a multiple of 128 take the tiled contraction (msa_route_gemm.hip;
 // the choice depends on M alone, so a query gives the same scores alone or in
 // a batch); otherwise up to 8 rows in all take the VALU scan and more the
 // batched MFMA scan. A query whose rows span several row tiles needs the

@@ -257,7 +257,7 @@ int launch_scan_mfma(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRb
                      int64_t n_chunks, int32_t token_reduce, float* out, hipStream_t s);
 int launch_parts_combine(const float* P, const RouteGeom& g, int64_t n_chunks,
                          int32_t token_reduce, float* S, hipStream_t s);
-// Tiled contraction scan (msa_route_gemm.hip) for M a multiple of 256: writes
+// Tiled contraction scan (msa_route_gemm.hip) for M a multiple of 128: writes
 // final scores (parts == 1) or P[parts][B][C]; ws is scan_gemm_ws_bytes of
 // workspace (the normalised query rows, and with many row tiles the
 // normalised keys).

@@ -9,8 +9,11 @@
 // a max (or sum) over each query's rows (section M, Memory Parallel bullet:
 // the score matrix is computed in tiles and never held whole).
 //
-// Used when M is a multiple of 256 (every 256-row tile then belongs to one
-// query; a 128-token query would leave half of each tile's products unused).
+// Used when M is a multiple of 128: 256-row tiles when M is a multiple of
+// 256, else 128-row tiles (every row tile then belongs to one query; a
+// 256-row tile over a 128-token query would leave half its products unused).
+// The kernels below are written for 256-row tiles; with 128-row tiles each
+// wave has two 32-row blocks instead of four, and nothing else changes.
 // Design:
 //   - qhat_rows_kernel writes q̂ once per call (fp64 norm per (row, head),
 //     the scaled value formed in fp32 and rounded to bf16);
@@ -60,8 +63,8 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// Reduces each chunk column's 128 rows of a wave tile: this lane's 64
-// accumulator values of the column (row blocks 0..3 × 16, in that order),
+// Reduces each chunk column's 32·kRB rows of a wave tile: this lane's 16·kRB
+// accumulator values of the column (row blocks 0..kRB-1 × 16, in that order),
 // then the other lane half's through one exchange. A sum for the mean
 // reduction; for the max, a maximum that is NaN when any value is. The max
 // takes fmaxf (which skips NaN) and carries a NaN through a running sum of
@@ -69,15 +72,15 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
 // unit vectors, |value| <= 8 up to rounding), so that sum is NaN exactly when
 // one of them is. Both branches are straight-line code (the branch is
 // uniform), so the epilogue costs one or two VALU operations per value.
-template <int kNcb>
-__device__ __forceinline__ void reduce_columns(const f32x16_t (&acc)[4][kNcb], bool mean,
+template <int kRB, int kNcb>
+__device__ __forceinline__ void reduce_columns(const f32x16_t (&acc)[kRB][kNcb], bool mean,
                                                int half, float (&red)[kNcb]) {
   if (mean) {
 #pragma unroll
     for (int cb = 0; cb < kNcb; ++cb) {
       float r = acc[0][cb][0];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
         for (int v = (rb == 0 ? 1 : 0); v < 16; ++v) r += acc[rb][cb][v];
       const float o = __shfl_xor(r, 32);
@@ -88,7 +91,7 @@ __device__ __forceinline__ void reduce_columns(const f32x16_t (&acc)[4][kNcb], b
     for (int cb = 0; cb < kNcb; ++cb) {
       float r = acc[0][cb][0], z = r;
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
         for (int v = (rb == 0 ? 1 : 0); v < 16; ++v) {
           r = fmaxf(r, acc[rb][cb][v]);
@@ -142,12 +145,12 @@ __global__ __launch_bounds__(256) void qhat_rows_kernel(const uint16_t* __restri
 struct GemmGeom {
   int32_t B, M;
   int64_t n_rows;        // B · M
-  int32_t n_row_tiles;   // n_rows / 256
+  int32_t n_row_tiles;   // n_rows / tile rows (256, or 128 when M is an odd multiple of 128)
   int32_t n_col_tiles;   // ceil(n_chunks / kCols)
-  int32_t parts;         // 256-row tiles per query (1: final scores)
+  int32_t parts;         // row tiles per query (1: final scores)
 };
 
-template <int kCols>
+template <int kRows, int kCols>
 __global__ __launch_bounds__(kGThreads) void scan_gemm_kernel(const uint16_t* __restrict__ Qh,
                                                               GemmGeom g,
                                                               const uint4* __restrict__ KR,
@@ -155,10 +158,12 @@ __global__ __launch_bounds__(kGThreads) void scan_gemm_kernel(const uint16_t* __
                                                               int32_t token_reduce,
                                                               float* __restrict__ out) {
   constexpr int kNcb = kCols / 128;                 // 32-chunk column blocks per wave
+  constexpr int kRB = kRows / 64;                   // 32-row blocks per wave
+  constexpr int kQPass = kRows / 32;                // staging passes of the q̂ tile
   constexpr int kBPass = kCols / 32;                // staging passes of the key tile
   extern __shared__ uint4 lds4[];
-  uint16_t* As = reinterpret_cast<uint16_t*>(lds4);          // [256][kGPitch] q̂ of one head
-  uint16_t* Bs = As + kGRows * kGPitch;                       // [kCols][kGPitch] k̂ of one head
+  uint16_t* As = reinterpret_cast<uint16_t*>(lds4);          // [kRows][kGPitch] q̂ of one head
+  uint16_t* Bs = As + kRows * kGPitch;                        // [kCols][kGPitch] k̂ of one head
 
   const int L = blockIdx.x;
   const int Y = g.n_row_tiles;
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(kGThreads) void scan_gemm_kernel(const uint16_t* __
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
-  const int wr = wave & 1;                  // row half
+  const int wr = wave & 1;                  // row half (kRows / 2 rows)
   const int wc = wave >> 1;                 // column quarter
 
   // staging: thread (r0, p) = (tid / 16, tid % 16) moves 16-byte piece p of
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(kGThreads) void scan_gemm_kernel(const uint16_t* __
   const int p = tid & 15;
   const int r0 = tid >> 4;
   const int64_t c_base = (int64_t)x * kCols;
-  const int64_t row_base = (int64_t)y * kGRows;
+  const int64_t row_base = (int64_t)y * kRows;
   // Each load is the tile's base (uniform) plus a 32-bit per-thread offset
   // (a tile spans at most 512 KiB). Chunks past the end read the last chunk
   // (clamped); their results are not stored.
@@ -203,12 +208,12 @@ __global__ __launch_bounds__(kGThreads) void scan_gemm_kernel(const uint16_t* __
   int koff[kBPass];
 #pragma unroll
   for (int i = 0; i < kBPass; ++i) koff[i] = min(r0 + 32 * i, k_rows - 1) * kRowV + p;
-  u32x4_t qreg[8], kreg[kBPass];
+  u32x4_t qreg[kQPass], kreg[kBPass];
   auto load = [&](int h) {
     const u32x4_t* qh = qtile + h * (kDim / 8);
     const u32x4_t* kh = ktile + h * (kDim / 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qreg[i] = qh[(r0 + 32 * i) * kRowV + p];
+    for (int i = 0; i < kQPass; ++i) qreg[i] = qh[(r0 + 32 * i) * kRowV + p];
 #pragma unroll
     for (int i = 0; i < kBPass; ++i) kreg[i] = kh[koff[i]];
   };
@@ -230,16 +235,16 @@ __global__ __launch_bounds__(kGThreads) void scan_gemm_kernel(const uint16_t* __
   };
   auto store = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < kQPass; ++i)
       *reinterpret_cast<u32x4_t*>(As + (r0 + 32 * i) * kGPitch + p * 8) = qreg[i];
 #pragma unroll
     for (int i = 0; i < kBPass; ++i)
       *reinterpret_cast<u32x4_t*>(Bs + (r0 + 32 * i) * kGPitch + p * 8) = kreg[i];
   };
 
-  f32x16_t acc[4][kNcb];
+  f32x16_t acc[kRB][kNcb];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < kNcb; ++cb)
 #pragma unroll
@@ -250,9 +255,9 @@ __global__ __launch_bounds__(kGThreads) void scan_gemm_kernel(const uint16_t* __
   store();
   __syncthreads();
 
-  // fragment rows of this wave: A rows 128·wr + 32·rb + col, B rows
+  // fragment rows of this wave: A rows (kRows/2)·wr + 32·rb + col, B rows
   // (chunks) wc·(kCols/4) + 32·cb + col; k slice 16·ks + 8·half
-  const uint16_t* a_base = As + (wr * 128 + col) * kGPitch + half * 8;
+  const uint16_t* a_base = As + (wr * (kRows / 2) + col) * kGPitch + half * 8;
   const uint16_t* b_base = Bs + (wc * (kCols / 4) + col) * kGPitch + half * 8;
 
   for (int h = 0; h < kHeads; ++h) {
@@ -262,15 +267,15 @@ __global__ __launch_bounds__(kGThreads) void scan_gemm_kernel(const uint16_t* __
       // the next head's keys are normalised half way through this head's
       // products, so their VALU work overlaps the MFMA pipeline
       if (ks == kDim / 32 && h + 1 < kHeads) normalise();
-      u32x4_t a[4], b[kNcb];
+      u32x4_t a[kRB], b[kNcb];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < kRB; ++rb)
         a[rb] = *reinterpret_cast<const u32x4_t*>(a_base + rb * 32 * kGPitch + ks * 16);
 #pragma unroll
       for (int cb = 0; cb < kNcb; ++cb)
         b[cb] = *reinterpret_cast<const u32x4_t*>(b_base + cb * 32 * kGPitch + ks * 16);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < kNcb; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[rb]), as_bf16x8(b[cb]),
@@ -283,10 +288,10 @@ __global__ __launch_bounds__(kGThreads) void scan_gemm_kernel(const uint16_t* __
     }
   }
 
-  // ---- epilogue: reduce this wave's 128 rows per chunk column
+  // ---- epilogue: reduce this wave's kRows / 2 rows per chunk column
   const bool mean = token_reduce == MSA_TOKEN_REDUCE_MEAN;
   float red[kNcb];
-  reduce_columns<kNcb>(acc, mean, half, red);
+  reduce_columns<kRB, kNcb>(acc, mean, half, red);
   // the two row halves are one query: half 1 hands its values to half 0,
   // which writes the tile's part (query y / parts, part y % parts)
   const float fin = (mean && g.parts == 1) ? 0.125f / (float)g.M : 0.125f;   // with the head mean
@@ -510,7 +515,7 @@ __global__ __launch_bounds__(kGThreads) void scan_gemm_dma_kernel(const uint16_t
   // ---- epilogue: as in scan_gemm_kernel
   const bool mean = token_reduce == MSA_TOKEN_REDUCE_MEAN;
   float red[kNcb];
-  reduce_columns<kNcb>(acc, mean, half, red);
+  reduce_columns<4, kNcb>(acc, mean, half, red);
   const float fin = (mean && g.parts == 1) ? 0.125f / (float)g.M : 0.125f;
   float* xch = reinterpret_cast<float*>(buf0);
   if (wr == 1 && half == 0) {
@@ -529,23 +534,40 @@ __global__ __launch_bounds__(kGThreads) void scan_gemm_dma_kernel(const uint16_t
   }
 }
 
-template <int kCols>
+template <int kRows, int kCols>
 constexpr size_t gemm_lds_bytes() {
-  return (size_t)(kGRows + kCols) * kGPitch * 2;
+  return (size_t)(kRows + kCols) * kGPitch * 2;
 }
 
 }  // namespace
 
-bool scan_gemm_fits(int32_t M) { return M >= kGRows && M % kGRows == 0; }
+template <int kRows, int kCols>
+static int launch_tiles(dim3 grid, const uint16_t* qhat, const GemmGeom& g, const uint4* kr,
+                        int64_t n_chunks, int32_t token_reduce, float* out, hipStream_t s) {
+  const void* fn = reinterpret_cast<const void*>(scan_gemm_kernel<kRows, kCols>);
+  constexpr size_t lds = gemm_lds_bytes<kRows, kCols>();
+  MSA_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+  hipLaunchKernelGGL((scan_gemm_kernel<kRows, kCols>), grid, dim3(kGThreads), lds, s, qhat, g, kr,
+                     n_chunks, token_reduce, out);
+  MSA_LAUNCH_CHECK("scan_gemm_kernel launch");
+  return MSA_OK;
+}
 
-int32_t scan_gemm_parts(int32_t M) { return M / kGRows; }
+// Row tiles of 256 when M is a multiple of 256, else 128 (a 128-row tile has
+// half the products per key byte, but a 256-row tile would leave half of its
+// products unused).
+static int32_t gemm_tile_rows(int32_t M) { return M % kGRows == 0 ? kGRows : kGRows / 2; }
+
+bool scan_gemm_fits(int32_t M) { return M >= kGRows / 2 && M % (kGRows / 2) == 0; }
+
+int32_t scan_gemm_parts(int32_t M) { return M / gemm_tile_rows(M); }
 
 // The staged form is used from kKhatMinTiles row tiles on: its k̂ pass
 // (a read and a write of the key store) then costs a few percent of the
 // contraction, while for one or two 256-row tiles it would cost as much.
 constexpr int32_t kKhatMinTiles = 4;
 static bool gemm_staged(int32_t B, int32_t M) {
-  return (int64_t)B * M / kGRows >= kKhatMinTiles;
+  return M % kGRows == 0 && (int64_t)B * M / kGRows >= kKhatMinTiles;
 }
 
 size_t scan_gemm_ws_bytes(int32_t B, int32_t M, int64_t n_chunks) {
@@ -559,13 +581,14 @@ int launch_scan_gemm(const uint16_t* QR, int32_t B, int32_t M, const uint16_t* K
                      hipStream_t s) {
   uint16_t* qhat = static_cast<uint16_t*>(ws);
   if (n_chunks == 0 || B == 0) return MSA_OK;
-  if (!scan_gemm_fits(M)) return fail(MSA_ERR_UNSUPPORTED, "tiled scan needs M a multiple of 256");
+  if (!scan_gemm_fits(M)) return fail(MSA_ERR_UNSUPPORTED, "tiled scan needs M a multiple of 128");
+  const int32_t rows = gemm_tile_rows(M);
   GemmGeom g;
   g.B = B;
   g.M = M;
   g.n_rows = (int64_t)B * M;
-  if (g.n_rows / kGRows > 0x7fffffffLL) return fail(MSA_ERR_SHAPE, "tiled scan: too many rows");
-  g.n_row_tiles = (int32_t)(g.n_rows / kGRows);
+  if (g.n_rows / rows > 0x7fffffffLL) return fail(MSA_ERR_SHAPE, "tiled scan: too many rows");
+  g.n_row_tiles = (int32_t)(g.n_rows / rows);
   g.parts = scan_gemm_parts(M);
   const int64_t qthreads = g.n_rows * kHeads;
   hipLaunchKernelGGL(qhat_rows_kernel, dim3((unsigned)((qthreads + 255) / 256)), dim3(256), 0, s,
@@ -594,21 +617,12 @@ int launch_scan_gemm(const uint16_t* QR, int32_t B, int32_t M, const uint16_t* K
     MSA_LAUNCH_CHECK("scan_gemm_dma_kernel launch");
     return MSA_OK;
   }
-  if (wide) {
-    MSA_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(scan_gemm_kernel<256>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)gemm_lds_bytes<256>()));
-    hipLaunchKernelGGL(scan_gemm_kernel<256>, dim3((unsigned)n_wg), dim3(kGThreads),
-                       gemm_lds_bytes<256>(), s, qhat, g, kr, n_chunks, token_reduce, out);
-  } else {
-    MSA_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(scan_gemm_kernel<128>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)gemm_lds_bytes<128>()));
-    hipLaunchKernelGGL(scan_gemm_kernel<128>, dim3((unsigned)n_wg), dim3(kGThreads),
-                       gemm_lds_bytes<128>(), s, qhat, g, kr, n_chunks, token_reduce, out);
-  }
-  MSA_LAUNCH_CHECK("scan_gemm_kernel launch");
-  return MSA_OK;
+  const dim3 grid((unsigned)n_wg);
+  if (rows == kGRows)
+    return wide ? launch_tiles<kGRows, 256>(grid, qhat, g, kr, n_chunks, token_reduce, out, s)
+                : launch_tiles<kGRows, 128>(grid, qhat, g, kr, n_chunks, token_reduce, out, s);
+  return wide ? launch_tiles<kGRows / 2, 256>(grid, qhat, g, kr, n_chunks, token_reduce, out, s)
+              : launch_tiles<kGRows / 2, 128>(grid, qhat, g, kr, n_chunks, token_reduce, out, s);
 }
 
 }  // namespace msa

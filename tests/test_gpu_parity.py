@@ -627,14 +627,16 @@ def test_route_long_queries_mean(B, M):
 
 
 @pytest.mark.parametrize("n_chunks", [1, 127, 129, 3001])
-@pytest.mark.parametrize("B,M", [(1, 256), (3, 256), (2, 512), (1, 768), (5, 256), (9, 512)])
+@pytest.mark.parametrize("B,M", [(1, 256), (3, 256), (2, 512), (1, 768), (5, 256), (9, 512),
+                                 (1, 128), (2, 384), (5, 128), (3, 640)])
 def test_route_tiled_scan(n_chunks, B, M):
     """Queries of whole 256-token tiles take the tiled contraction scan: one
     tile per query (the two row halves merged in the workgroup), and two or
     three tiles per query folded by the second kernel, with chunk counts that
     fill no 128- or 256-chunk tile or end mid-tile. Four or more row tiles
     take the blocked workgroup order (5 and 18 row tiles leave its last block
-    part empty)."""
+    part empty). Queries that are an odd multiple of 128 tokens take 128-row
+    tiles (one, three or five per query)."""
     _banner(f"route tiled n_chunks={n_chunks} B={B} M={M}")
     st = _store(n_chunks, 900 + n_chunks, lo=1, hi=7)
     QR = synth.randn_bf16((B, M, 8, 128), synth.torch_gen(14, n_chunks * 1000 + B * 300 + M))
@@ -705,7 +707,7 @@ def test_route_tiled_scan_nan(token_reduce):
         assert torch.equal(S[0][torch.from_numpy(keep)], clean[0][torch.from_numpy(keep)])
 
 
-@pytest.mark.parametrize("B,M", [(2, 256), (3, 512)])
+@pytest.mark.parametrize("B,M", [(2, 256), (3, 512), (2, 128), (1, 384)])
 def test_route_tiled_scan_mean(B, M):
     _banner(f"route tiled MEAN B={B} M={M}")
     st = _store(2500, 37)
