@@ -225,7 +225,8 @@ def _check_route(QR, st, d, accumulate=False, prev=None):
 
 
 @pytest.mark.parametrize("B,M", [(1, 1), (3, 1), (2, 3), (1, 8), (5, 13), (1, 64), (9, 1),
-                                 (64, 1), (1, 130), (3, 70), (70, 1)])
+                                 (64, 1), (1, 130), (3, 70), (70, 1), (5, 2), (3, 4), (40, 2),
+                                 (17, 4), (129, 1)])
 def test_route_shapes(B, M):
     _banner(f"route B={B} M={M}")
     st = _store(3000, 21 + B * 100 + M)
@@ -247,7 +248,7 @@ def test_route_cfg1_planted():
     assert set(ids.cpu().numpy()[0][:4].tolist()) == set(mem.planted.keys())
 
 
-@pytest.mark.parametrize("B,M", [(2, 11), (1, 3), (2, 100)])
+@pytest.mark.parametrize("B,M", [(2, 11), (1, 3), (2, 100), (6, 2), (20, 4)])
 def test_route_mean_mode(B, M):
     _banner(f"route MEAN B={B} M={M}")
     st = _store(2000, 31)
@@ -595,7 +596,7 @@ def test_select_topk_fallback_paths(case):
 
 
 @pytest.mark.parametrize("n_chunks", [1, 2, 5, 31, 33, 3001])
-@pytest.mark.parametrize("B,M", [(1, 1), (9, 1), (2, 13)])
+@pytest.mark.parametrize("B,M", [(1, 1), (9, 1), (2, 13), (33, 2)])
 def test_route_ragged_chunk_counts(n_chunks, B, M):
     """Chunk counts that fill no tile, end mid-tile, or are not a multiple of
     four, on both scans (8 rows or fewer: VALU; more: MFMA)."""
@@ -705,6 +706,37 @@ def test_route_tiled_scan_nan(token_reduce):
         assert np.isnan(s[1]).all()
         assert np.isnan(s[0][nan_cols]).all()
         assert torch.equal(S[0][torch.from_numpy(keep)], clean[0][torch.from_numpy(keep)])
+
+
+@pytest.mark.parametrize("token_reduce", [O.TOKEN_REDUCE_MAX, O.TOKEN_REDUCE_MEAN])
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_route_short_queries_nan(token_reduce, M):
+    """Many short queries on the batched MFMA scan (B·M > 8, M = 1, 2 or 4,
+    B·M just over a multiple of 64): a NaN key element makes that chunk's
+    score NaN for every query, a NaN in one row of one query makes that
+    query's scores NaN, and every other score equals the NaN-free run's bit
+    for bit."""
+    B, C = 65 // M + 1, 3001
+    _banner(f"route short queries NaN B={B} M={M} reduce={token_reduce}")
+    st = _store(C, 47)
+    d = msa.dims(token_reduce=token_reduce)
+    QR = synth.randn_bf16((B, M, 8, 128), synth.torch_gen(19, M * 10 + token_reduce))
+    KR = st.KRbar.clone()
+    clean = msa.route_scores(QR.to(DEV), KR.to(DEV), d).cpu()
+    nan_cols = [0, 77, C - 1]
+    for c in nan_cols:
+        KR[c, 3, 100] = float("nan")
+    bad_q = B - 2
+    QRn = QR.clone()
+    QRn[bad_q, M - 1, 5, 9] = float("nan")
+    S = msa.route_scores(QRn.to(DEV), KR.to(DEV), d).cpu()
+    torch.cuda.synchronize()
+    s = S.numpy()
+    assert np.isnan(s[bad_q]).all()
+    assert np.isnan(s[:, nan_cols]).all()
+    keep_q = [b for b in range(B) if b != bad_q]
+    keep_c = torch.from_numpy(np.setdiff1d(np.arange(C), nan_cols))
+    assert torch.equal(S[keep_q][:, keep_c], clean[keep_q][:, keep_c])
 
 
 @pytest.mark.parametrize("B,M", [(2, 256), (3, 512), (2, 128), (1, 384)])
