@@ -300,7 +300,7 @@ int32_t msa_interleave_step(const msa_dims* d, msa_interleave_state* st, const m
  * results equal B msa_interleave_step calls on the same inputs bit for bit
  * when M_new > 8 (a single query of at most 8 rows takes the fp32-exact VALU
  * scan instead, which may differ in the last bits). Buffers belong to the
- * caller:
+ * caller (1 <= B <= 65535, MSA_ERR_SHAPE otherwise):
  *   doc_scores [B, n_docs] fp32 (msa_interleave_batch_reset sets -inf);
  *   K_loc, V_loc [B, cap_loc, n_kv_heads, 128] bf16, query b's rows at
  *     b * cap_loc; every query holds n_loc tokens (host value, advanced by

@@ -1,6 +1,7 @@
 // C entry points of the MSA library: argument validation, workspace layout,
 // kernel selection and error reporting. Every check runs before anything is
 // enqueued, so a failed call leaves outputs untouched.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -222,6 +223,43 @@ int check_attend_args(const msa_dims* d, const msa_bf16* Q, int32_t M, const msa
   MSA_A16("attend", Kbar);
   MSA_A16("attend", Vbar);
   MSA_A16("attend", out);
+  return MSA_OK;
+}
+
+// Memory Interleave appends each query's new K and V rows to its local
+// context: nb queries' rows [0, n_vec) (16-byte vectors) of src + b·src_stride
+// go to dst + b·dst_stride, K and V in one launch (blockIdx.y: 0 = K, 1 = V,
+// blockIdx.z: query). One launch for a whole batched round instead of a copy
+// call per query and tensor (each a kernel of its own, ~4 µs apiece).
+__global__ __launch_bounds__(256) void append_rows_kernel(const uint4* __restrict__ K_src,
+                                                          const uint4* __restrict__ V_src,
+                                                          uint4* __restrict__ K_dst,
+                                                          uint4* __restrict__ V_dst, int64_t n_vec,
+                                                          int64_t src_stride, int64_t dst_stride) {
+  const int64_t b = blockIdx.z;
+  const uint4* src = (blockIdx.y ? V_src : K_src) + b * src_stride;
+  uint4* dst = (blockIdx.y ? V_dst : K_dst) + b * dst_stride;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+// Rows [0, M_new) of query b's K_new / V_new (query stride M_new rows) to rows
+// [n_loc, n_loc + M_new) of its local buffers (query stride cap_loc rows).
+int launch_append_rows(const msa_bf16* K_new, const msa_bf16* V_new, msa_bf16* K_loc,
+                       msa_bf16* V_loc, int32_t B, int32_t M_new, int32_t n_loc,
+                       int32_t cap_loc, hipStream_t s) {
+  constexpr int64_t kRowVec = kRowElems * 2 / 16;        // 16-byte vectors per KV row
+  const int64_t n_vec = (int64_t)M_new * kRowVec;
+  if (B > 65535) return fail(MSA_ERR_SHAPE, "interleave: B=%d exceeds 65535 queries", B);
+  if (B < 1 || n_vec < 1) return MSA_OK;
+  const int64_t blocks = std::min<int64_t>((n_vec + 255) / 256, 1024);
+  const int64_t at = (int64_t)n_loc * kRowVec;
+  hipLaunchKernelGGL(append_rows_kernel, dim3((unsigned)blocks, 2, (unsigned)B), dim3(256), 0, s,
+                     reinterpret_cast<const uint4*>(K_new), reinterpret_cast<const uint4*>(V_new),
+                     reinterpret_cast<uint4*>(K_loc) + at, reinterpret_cast<uint4*>(V_loc) + at,
+                     n_vec, n_vec, (int64_t)cap_loc * kRowVec);
+  MSA_LAUNCH_CHECK("append_rows_kernel launch");
   return MSA_OK;
 }
 
@@ -478,11 +516,8 @@ int32_t msa_interleave_step(const msa_dims* d, msa_interleave_state* st, const m
   rc = route_topk_impl(d, QR_new, 1, M_new, KRbar, dco, n_docs, n_chunks, st->doc_scores, 1,
                        st->topk_ids, st->topk_scores, st->n_sel, ws, ws_bytes, s);
   if (rc) return rc;
-  const size_t row_bytes = (size_t)kRowElems * 2;
-  MSA_HIP(hipMemcpyAsync(st->K_loc + (size_t)st->n_loc * kRowElems, K_new, row_bytes * M_new,
-                         hipMemcpyDeviceToDevice, s));
-  MSA_HIP(hipMemcpyAsync(st->V_loc + (size_t)st->n_loc * kRowElems, V_new, row_bytes * M_new,
-                         hipMemcpyDeviceToDevice, s));
+  rc = launch_append_rows(K_new, V_new, st->K_loc, st->V_loc, 1, M_new, st->n_loc, st->cap_loc, s);
+  if (rc) return rc;
   AttendArgs a;
   a.Q = Q_new; a.M = M_new; a.n_q_heads = d->n_q_heads;
   a.K_loc = st->K_loc; a.V_loc = st->V_loc; a.M_loc = M_loc; a.k_loc_rotated = 0;
@@ -553,7 +588,8 @@ int32_t msa_interleave_batch_step(const msa_dims* d, msa_interleave_batch* st,
   if (!Q_new || !K_new || !V_new || !QR_new)
     return fail(MSA_ERR_INVALID_ARG, "interleave_batch: NULL input");
   const int32_t B = st->B;
-  if (B < 1) return fail(MSA_ERR_SHAPE, "interleave_batch: B=%d must be >= 1", B);
+  if (B < 1 || B > 65535)
+    return fail(MSA_ERR_SHAPE, "interleave_batch: B=%d must be in [1, 65535]", B);
   if (M_new < 1 || st->n_loc < 0 || (int64_t)st->n_loc + M_new > st->cap_loc)
     return fail(MSA_ERR_SHAPE, "interleave_batch: n_loc (%d) + M_new (%d) exceeds cap_loc (%d)",
                 st->n_loc, M_new, st->cap_loc);
@@ -587,14 +623,8 @@ int32_t msa_interleave_batch_step(const msa_dims* d, msa_interleave_batch* st,
   if (rc) return rc;
   const size_t row = (size_t)kRowElems;                       // elements per KV token row
   const size_t q_row = (size_t)d->n_q_heads * kDim;           // elements per query token row
-  for (int32_t b = 0; b < B; ++b) {
-    msa_bf16* kl = st->K_loc + (size_t)b * st->cap_loc * row;
-    msa_bf16* vl = st->V_loc + (size_t)b * st->cap_loc * row;
-    MSA_HIP(hipMemcpyAsync(kl + (size_t)st->n_loc * row, K_new + (size_t)b * M_new * row,
-                           row * 2 * M_new, hipMemcpyDeviceToDevice, s));
-    MSA_HIP(hipMemcpyAsync(vl + (size_t)st->n_loc * row, V_new + (size_t)b * M_new * row,
-                           row * 2 * M_new, hipMemcpyDeviceToDevice, s));
-  }
+  rc = launch_append_rows(K_new, V_new, st->K_loc, st->V_loc, B, M_new, st->n_loc, st->cap_loc, s);
+  if (rc) return rc;
   // queries go through the attention launches in groups of grp (one group
   // per set of launches when the multi-token kernel serves the shape)
   for (int32_t b = 0; b < B; b += grp) {

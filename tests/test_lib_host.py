@@ -199,8 +199,9 @@ def test_route_topk_noalloc_rejects_calls_beyond_its_scratch():
 
 def test_interleave_batch_rejects_bad_states_before_the_gpu():
     """The batched interleave calls check the state and shapes on the host:
-    a batch of no queries, a round past the local capacity and missing
-    buffers fail with their codes and touch no device memory."""
+    a batch of no queries or of more than 65,535, a round past the local
+    capacity and missing buffers fail with their codes and touch no device
+    memory."""
     L = msa.lib()
     d = msa.dims()
     p = ctypes.c_void_p(16)
@@ -208,6 +209,9 @@ def test_interleave_batch_rejects_bad_states_before_the_gpu():
     assert L.msa_interleave_batch_reset(ctypes.byref(st), 10, None) == -2
     args = (p, p, p, p, 8, p, p, p, 0, 100, p, 10, 64, p, p, 1 << 20, None)
     assert L.msa_interleave_batch_step(ctypes.byref(d), ctypes.byref(st), *args) == -2
+    st.B = 65536                           # one launch appends every query's rows: B <= 65535
+    assert L.msa_interleave_batch_step(ctypes.byref(d), ctypes.byref(st), *args) == -2
+    assert b"65535" in L.msa_last_error()
     st.B, st.n_loc = 2, 60                 # 60 + 8 tokens exceed cap_loc = 64
     assert L.msa_interleave_batch_step(ctypes.byref(d), ctypes.byref(st), *args) == -2
     assert b"cap_loc" in L.msa_last_error()
