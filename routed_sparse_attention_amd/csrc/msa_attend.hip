@@ -595,9 +595,13 @@ struct MtArgs {
 };
 
 // Rotates the query rows (at pos0 + M_loc - M + u, then scaled by qscale) and,
-// when Kr != nullptr, the local keys (at pos0 + v) into the workspace: one
-// thread per rotation pair, the angle reduced to [-1/2, 1/2] revolutions in
-// fp64, hardware fp32 cos/sin, bf16 result.
+// when Kr != nullptr, the local keys (at pos0 + v) into the workspace. One
+// wave per (token, group of 8 heads), lane m = rotation pair (m, m + 64): the
+// angle depends on the token's position and m only, so a wave forms its
+// (cos, sin) once — the angle reduced to [-1/2, 1/2] revolutions in fp64,
+// hardware fp32 cos/sin — and applies it to its 8 heads (each head's two
+// loads are one 128-byte run per wave); bf16 results.
+constexpr int kRotHeads = 8;
 __global__ __launch_bounds__(256) void rot_qk_kernel(const uint16_t* __restrict__ Q, int32_t M,
                                                      int32_t Hq, const uint16_t* __restrict__ Kl,
                                                      int32_t M_loc, const int32_t* __restrict__ n_sel,
@@ -606,42 +610,52 @@ __global__ __launch_bounds__(256) void rot_qk_kernel(const uint16_t* __restrict_
                                                      uint16_t* __restrict__ Kr, int32_t nb,
                                                      int64_t q_stride, int64_t kl_stride) {
   // nb queries: query b's Q at Q + b·q_stride, its local keys at
-  // Kl + b·kl_stride, its n_sel at n_sel[b]; outputs packed per query
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t nq = (int64_t)M * Hq * (kDim / 2);
-  const int64_t nk = Kr ? (int64_t)M_loc * kHeads * (kDim / 2) : 0;
-  if (idx >= (nq + nk) * nb) return;
+  // Kl + b·kl_stride, its n_sel at n_sel[b]; outputs packed per query.
+  // Units: per query, M tokens × Hq / 8 query head groups, then (with Kr)
+  // M_loc tokens of 8 KV heads.
+  const int64_t unit = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int m = threadIdx.x & 63;
+  const int n_qg = Hq / kRotHeads;
+  const int64_t nq = (int64_t)M * n_qg;
+  const int64_t nk = Kr ? (int64_t)M_loc : 0;
+  if (unit >= (nq + nk) * nb) return;
   const uint16_t* src;
   uint16_t* dst;
-  int64_t row, pos;
-  int m, b;
+  int64_t row0, pos;
+  int b;
   float sc = 1.0f;
-  if (idx < nq * nb) {
-    b = (int)(idx / nq);
-    const int64_t j = idx - (int64_t)b * nq;
-    row = j / (kDim / 2);
-    m = (int)(j % (kDim / 2));
+  const bool is_q = unit < nq * nb;
+  if (is_q) {
+    b = (int)(unit / nq);
+    const int64_t j = unit - (int64_t)b * nq;
+    const int64_t tok = j / n_qg;
+    row0 = tok * Hq + (j % n_qg) * kRotHeads;      // first of the group's rows
     src = Q + b * q_stride;
     dst = Qr + (int64_t)b * M * Hq * kDim;
     sc = qscale;
+    pos = (M_loc - M) + tok;
   } else {
-    const int64_t j0 = idx - nq * nb;
+    const int64_t j0 = unit - nq * nb;
     b = (int)(j0 / nk);
-    const int64_t j = j0 - (int64_t)b * nk;
-    row = j / (kDim / 2);
-    m = (int)(j % (kDim / 2));
+    const int64_t tok = j0 - (int64_t)b * nk;
+    row0 = tok * kHeads;
     src = Kl + b * kl_stride;
     dst = Kr + (int64_t)b * M_loc * kHeads * kDim;
+    pos = tok;
   }
-  const int64_t pos0 = pos0_arg < 0 ? (int64_t)clamp_nsel(n_sel + b, top_k) : pos0_arg;
-  if (idx < nq * nb)
-    pos = pos0 + (M_loc - M) + row / Hq;
-  else
-    pos = pos0 + row / kHeads;
+  pos += pos0_arg < 0 ? (int64_t)clamp_nsel(n_sel + b, top_k) : pos0_arg;
   const float2 cs = cis_hw((double)pos * rt.om[m]);
-  const float x = bf16f(src[row * kDim + m]), y = bf16f(src[row * kDim + m + 64]);
-  dst[row * kDim + m] = f2bf((x * cs.x - y * cs.y) * sc);
-  dst[row * kDim + m + 64] = f2bf((y * cs.x + x * cs.y) * sc);
+  float x[kRotHeads], y[kRotHeads];
+#pragma unroll
+  for (int h = 0; h < kRotHeads; ++h) {
+    x[h] = bf16f(src[(row0 + h) * kDim + m]);
+    y[h] = bf16f(src[(row0 + h) * kDim + m + 64]);
+  }
+#pragma unroll
+  for (int h = 0; h < kRotHeads; ++h) {
+    dst[(row0 + h) * kDim + m] = f2bf((x[h] * cs.x - y[h] * cs.y) * sc);
+    dst[(row0 + h) * kDim + m + 64] = f2bf((y[h] * cs.x + x[h] * cs.y) * sc);
+  }
 }
 
 // LDS row of key q (0..63) of a tile in the K buffer: bits 2 and 3 swapped.
@@ -1076,9 +1090,10 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
     uint16_t* kr_dst = a.k_loc_rotated ? nullptr : Kr;
     const int64_t q_stride = batch ? batch->q_stride : 0;
     const int64_t kl_stride = batch ? batch->kv_stride : 0;
-    const int64_t pairs =
-        ((int64_t)a.M * a.n_q_heads + (kr_dst ? (int64_t)a.M_loc * kHeads : 0)) * (kDim / 2) * nb;
-    hipLaunchKernelGGL(rot_qk_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s,
+    // one wave (64 lanes) per token and group of 8 heads
+    const int64_t waves =
+        ((int64_t)a.M * (a.n_q_heads / kRotHeads) + (kr_dst ? (int64_t)a.M_loc : 0)) * nb;
+    hipLaunchKernelGGL(rot_qk_kernel, dim3((unsigned)((waves * 64 + 255) / 256)), dim3(256), 0, s,
                        a.Q, a.M, a.n_q_heads, a.K_loc, a.M_loc, a.n_sel, a.top_k, a.pos0, rt,
                        qk_scale_log2, Qr, kr_dst, nb, q_stride, kl_stride);
     MSA_LAUNCH_CHECK("rot_qk_kernel launch");
