@@ -152,12 +152,13 @@ int32_t msa_encode_pool(const msa_dims* d, const msa_bf16* K, const msa_bf16* V,
  *     in rank order; entries past n_sel are -1 / -inf.
  *   n_sel [B] int32 (written).
  *   Norms are clamped at 1e-6 before dividing; a NaN score ranks last.
- *   Precision: with at most 8 query rows in all the cosines are fp32-exact
- *     (q̂ kept as a bf16 hi + lo pair); with more rows q̂ is rounded to bf16,
- *     and when M is a multiple of 128 k̂ = k/‖k‖ is rounded to bf16 as well
+ *   Precision: with a single query row in all (decode) the cosines are
+ *     fp32-exact (q̂ kept as a bf16 hi + lo pair); with more rows q̂ is
+ *     rounded to bf16, and when M is a multiple of 128 k̂ = k/‖k‖ is rounded
+ *     to bf16 as well
  *     (the head sum is then one contraction); a chunk score moves by ~1e-4 at
- *     most. The path depends on B·M <= 8 and on M only, so a query of more
- *     than 8 tokens gets the same scores alone or in any batch (with 1024 or
+ *     most. The path depends on B·M == 1 and on M only, so a query of more
+ *     than one token gets the same scores alone or in any batch (with 1024 or
  *     more rows of whole 256-token tiles the contraction stages normalised
  *     keys written once per call, and runs the same products in the same
  *     order: the scores are bit-identical).
@@ -298,8 +299,8 @@ int32_t msa_interleave_step(const msa_dims* d, msa_interleave_state* st, const m
  * each query's top-k and attends each query's new tokens over its own
  * selection and local context. One scan launch covers every query's rows; the
  * results equal B msa_interleave_step calls on the same inputs bit for bit
- * when M_new > 8 (a single query of at most 8 rows takes the fp32-exact VALU
- * scan instead, which may differ in the last bits). Buffers belong to the
+ * when M_new > 1 (a single query of one row takes the fp32-exact VALU scan
+ * instead, which may differ in the last bits). Buffers belong to the
  * caller (1 <= B <= 65535, MSA_ERR_SHAPE otherwise):
  *   doc_scores [B, n_docs] fp32 (msa_interleave_batch_reset sets -inf);
  *   K_loc, V_loc [B, cap_loc, n_kv_heads, 128] bf16, query b's rows at

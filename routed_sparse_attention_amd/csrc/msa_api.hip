@@ -98,8 +98,8 @@ namespace {
 // Scan plan: kernel choice and the workspace it needs. Queries whose token
 // count M is a multiple of 128 take the tiled contraction (msa_route_gemm.hip;
 // the choice depends on M alone, so a query gives the same scores alone or in
-// a batch); otherwise up to 8 rows in all take the VALU scan and more the
-// batched MFMA scan. A query whose rows span several row tiles needs the
+// a batch); otherwise a single row in all (decode) takes the fp32-exact VALU
+// scan and more rows the batched MFMA scan. A query whose rows span several row tiles needs the
 // partials buffer; the tiled scan also needs the normalised query rows.
 enum ScanKind { kScanValu, kScanMfma, kScanGemm };
 struct ScanPlan {

@@ -249,7 +249,11 @@ __host__ __device__ inline TileRows tile_rows_of(const RouteGeom& g, int ty) {
 // Scan output: with parts == 1 the kernels write final chunk scores S[B][C]
 // (MEAN already divided by M); with parts > 1 they write per-part partials
 // P[parts][B][C] (max, or sums under MEAN) that launch_parts_combine folds.
-constexpr int kValuTileRows = 8;
+// The fp32-exact VALU scan serves one query row (decode); from two rows on the
+// batched MFMA scan streams the store faster (the VALU form's per-row lane
+// reductions make it ALU-bound: 8 rows over 1.56M chunks took 1.5 ms, the MFMA
+// scan 0.63 ms).
+constexpr int kValuTileRows = 1;
 constexpr int kMfmaTileRows = 16;   // one segment per MFMA lane group
 int launch_scan_valu(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRbar,
                      int64_t n_chunks, int32_t token_reduce, float* out, hipStream_t s);

@@ -14,7 +14,9 @@
 //     max(‖Q^R‖, eps) per head in fp64, split into bf16 hi + lo parts
 //     (q̂ ≈ hi + lo to ~2^-17), so bf16 products against the bf16 keys keep
 //     fp32-level accuracy.
-//   scan_valu (decode and small batches, <= 8 rows per tile): HBM-bound
+//   scan_valu (one query row: decode; the kernel is written for up to R
+//     rows, but past one row its per-row lane reductions make it ALU-bound
+//     and the plan sends such calls to the MFMA scan): HBM-bound
 //     stream, one chunk row (2 KiB) per wave per step. Lane l loads the 16-byte
 //     vectors l and 64+l of the row — each load instruction covers one
 //     contiguous KiB — i.e. dims [8(l%16), +8) of heads l/16 and 4 + l/16, and
@@ -204,14 +206,8 @@ int launch_scan_valu(const uint16_t* QR, const RouteGeom& g, const uint16_t* KRb
   int64_t wg = (n_chunks + per_wg - 1) / per_wg;
   if (wg > 8192) wg = 8192;
   const dim3 grid((unsigned)wg, (unsigned)g.n_tiles);
-  if (rows <= 1)
-    hipLaunchKernelGGL(scan_valu_kernel<1>, grid, dim3(256), 0, s, QR, g, kr, n_chunks, token_reduce, out);
-  else if (rows <= 2)
-    hipLaunchKernelGGL(scan_valu_kernel<2>, grid, dim3(256), 0, s, QR, g, kr, n_chunks, token_reduce, out);
-  else if (rows <= 4)
-    hipLaunchKernelGGL(scan_valu_kernel<4>, grid, dim3(256), 0, s, QR, g, kr, n_chunks, token_reduce, out);
-  else
-    hipLaunchKernelGGL(scan_valu_kernel<8>, grid, dim3(256), 0, s, QR, g, kr, n_chunks, token_reduce, out);
+  if (rows != 1) return fail(MSA_ERR_UNSUPPORTED, "VALU scan: %d rows (one expected)", rows);
+  hipLaunchKernelGGL(scan_valu_kernel<1>, grid, dim3(256), 0, s, QR, g, kr, n_chunks, token_reduce, out);
   MSA_LAUNCH_CHECK("scan_valu_kernel launch");
   return MSA_OK;
 }

@@ -42,7 +42,7 @@ def _close(gpu, ref, what, rel=2e-3):
 
 @pytest.mark.parametrize("B,M,n_docs,tau,seed", [
     (1, 1, 40, 0.05, 71),     # decode shape (VALU scan)
-    (2, 3, 30, 0.1, 72),      # small batch (VALU scan, 6 rows)
+    (2, 3, 30, 0.1, 72),      # small batch (MFMA scan, 6 rows)
     (12, 1, 50, 0.05, 73),    # batched single tokens (MFMA scan)
     (3, 17, 25, 0.2, 74),     # queries longer than one 16-row segment (MFMA, parts)
     (1, 40, 20, 0.5, 75),

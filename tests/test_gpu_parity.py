@@ -599,7 +599,7 @@ def test_select_topk_fallback_paths(case):
 @pytest.mark.parametrize("B,M", [(1, 1), (9, 1), (2, 13), (33, 2)])
 def test_route_ragged_chunk_counts(n_chunks, B, M):
     """Chunk counts that fill no tile, end mid-tile, or are not a multiple of
-    four, on both scans (8 rows or fewer: VALU; more: MFMA)."""
+    four, on both scans (one row: VALU; more: MFMA)."""
     _banner(f"route n_chunks={n_chunks} B={B} M={M}")
     st = _store(n_chunks, 500 + n_chunks, lo=1, hi=7)
     QR = synth.randn_bf16((B, M, 8, 128), synth.torch_gen(9, n_chunks * 100 + B * 10 + M))
