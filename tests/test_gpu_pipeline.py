@@ -90,3 +90,53 @@ def test_concurrent_queries_match_sequential():
                                   [int(x) for x in ids])
             assert_attn_close(O.bf16_to_f64(u16(conc[q]["out"][l])), ref,
                               f"lane {q} layer {l} attention")
+
+
+def test_batched_concurrent_queries_match_oracle():
+    """The batched schedule of concurrent decode queries: per layer the
+    queries are routed together (one scan of the layer's router keys and one
+    selection for all), then each attends over its own selection, and the next
+    layer follows. Query q's router rows at layer l are those of input layer
+    (l + q) % L, so the rows of a batch differ. Every query's document scores,
+    top-16 and attention are checked against the oracle."""
+    print("[case] 3 queries × 4 layers routed together per layer", flush=True)
+    L, Qn = 4, 3
+    store, queries, atts = synth.cfg4_100m(DEV, seed=82, n_chunks=30_000, n_layers=L,
+                                           kv_pinned=True)
+    d = msa.dims()
+    dco = torch.from_numpy(store.doc_chunk_offsets).to(DEV)
+    max_sel = d.top_k * int(np.diff(store.doc_chunk_offsets).max())
+    C, N = store.n_chunks, store.n_docs
+    S = torch.empty((Qn, C), dtype=torch.float32, device=DEV)
+    ds = torch.empty((Qn, N), dtype=torch.float32, device=DEV)
+    outs = (torch.empty((Qn, 16), dtype=torch.int32, device=DEV),
+            torch.empty((Qn, 16), dtype=torch.float32, device=DEV),
+            torch.empty((Qn,), dtype=torch.int32, device=DEV))
+    res = []
+    for l in range(L):
+        QR = torch.cat([queries[(l + q) % L].QR for q in range(Qn)])
+        msa.route_scores(QR, store.KRbar[l], d, out=S)
+        msa.select_topk(S, dco, d, doc_scores=ds, outs=outs)
+        out = [msa.sparse_attend(atts[l].Q, atts[l].K_loc, atts[l].V_loc, store.Kbar, store.Vbar,
+                                 dco, outs[0][q], outs[2][q:q + 1], max_sel, d=d)
+               for q in range(Qn)]
+        res.append((ds.clone(), outs[0].clone(), out))
+    torch.cuda.synchronize()
+    dco_h = store.doc_chunk_offsets
+    kb_h, vb_h = u16(store.Kbar), u16(store.Vbar)
+    a_ref = {}
+    for l in range(L):
+        ds_l, ids_l, out_l = res[l]
+        for q in range(Qn):
+            ref_s = O.doc_scores(O.chunk_scores(u16(queries[(l + q) % L].QR[0]),
+                                                u16(store.KRbar[l])), dco_h)
+            ids = ids_l[q].cpu().numpy()
+            assert_scores_close(ds_l[q].cpu().numpy(), ref_s, f"query {q} layer {l} doc scores")
+            assert_topk_matches(ids, 16, ref_s, 16)
+            a = atts[l]
+            key = (l, tuple(int(x) for x in ids))
+            if key not in a_ref:
+                a_ref[key] = O.sparse_attend(u16(a.Q), u16(a.K_loc), u16(a.V_loc), kb_h, vb_h,
+                                             dco_h, list(key[1]))
+            assert_attn_close(O.bf16_to_f64(u16(out_l[q])), a_ref[key],
+                              f"query {q} layer {l} attention")
