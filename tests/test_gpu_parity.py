@@ -489,10 +489,13 @@ def test_interleave_batch_equals_single_queries(B, M_new):
     batch = msa.InterleaveBatch(B, n_docs, cap_loc=3 * M_new, d=d)
     singles = [msa.Interleave(n_docs, cap_loc=3 * M_new, d=d) for _ in range(B)]
     st1 = O.InterleaveState(n_docs)
+    appended_k, appended_v = [], []
     for r in range(3):
         ins = [synth.cfg5_round(mem, chains[b][r], b, r, seed=11, M_new=M_new, block=64)
                for b in range(B)]
         QR, Q, Kn, Vn = (torch.stack([x[i] for x in ins]).to(DEV) for i in range(4))
+        appended_k.append(Kn)
+        appended_v.append(Vn)
         out = batch.step(Q, Kn, Vn, QR, Rb, Kb, Vb, dco, max_sel)
         outs = [singles[b].step(Q[b], Kn[b], Vn[b], QR[b], Rb, Kb, Vb, dco, max_sel)
                 for b in range(B)]
@@ -512,6 +515,13 @@ def test_interleave_batch_equals_single_queries(B, M_new):
                             st1.doc_scores, 4)
         assert_attn_close(O.bf16_to_f64(u16(out[1])), ref, f"round {r} attention")
     assert batch.n_loc == 3 * M_new
+    # one append launch per round filled each query's local context with its
+    # own rows, in round order, up to the capacity and no further
+    for b in range(B):
+        assert torch.equal(batch.K_loc[b], torch.cat([k[b] for k in appended_k]))
+        assert torch.equal(batch.V_loc[b], torch.cat([v[b] for v in appended_v]))
+        assert torch.equal(singles[b].K_loc, batch.K_loc[b])
+        assert torch.equal(singles[b].V_loc, batch.V_loc[b])
 
 
 # ---------------------------------------------------------------------------
