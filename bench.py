@@ -859,11 +859,14 @@ def pipeline_on(args, store, queries, atts, Qn):
     layers in order on its own stream; the Qn queries as one batch (per
     layer one routing scan and selection for all, then each attention, the
     next layer after them); and the same queries one after another on one
-    stream. Layer l + 1 of a query always runs after its layer l."""
+    stream. Layer l + 1 of a query always runs after its layer l. Every query
+    has inputs of its own at every layer (its own planted document, query
+    rows and local context), so the queries select different documents."""
     import numpy as np
     import torch
 
     import routed_sparse_attention_amd as msa
+    import synth
 
     dev = "cuda"
     L = len(queries)
@@ -871,9 +874,17 @@ def pipeline_on(args, store, queries, atts, Qn):
     d = msa.dims()
     dco = torch.from_numpy(store.doc_chunk_offsets).to(dev)
     max_sel = d.top_k * int(np.diff(store.doc_chunk_offsets).max())
+    M_loc = atts[0].K_loc.shape[0]
+    # per layer: Qn single-token router queries with one planted document
+    # each, and Qn decode queries' rows and local context
+    qsets = [synth.route_queries_planted_pooled(store, Qn, 1, 7000 + 100 * l, dev, layer=l)
+             for l in range(L)]
+    att_q = [[synth.attend_inputs(1, M_loc, 8000 + 100 * l + b, dev) for b in range(Qn)]
+             for l in range(L)]
 
-    class Lane:   # one query's buffers and stream (each query reuses the layer inputs)
-        def __init__(self):
+    class Lane:   # one query's buffers and stream
+        def __init__(self, b):
+            self.b = b
             self.stream = torch.cuda.Stream()
             self.S = torch.empty((1, C), dtype=torch.float32, device=dev)
             self.ds = torch.empty((1, N), dtype=torch.float32, device=dev)
@@ -886,10 +897,13 @@ def pipeline_on(args, store, queries, atts, Qn):
                 1, atts[0].K_loc.shape[0], max_sel, d), dtype=torch.uint8, device=dev)
             self.out = torch.empty((1, 32, 128), dtype=torch.bfloat16, device=dev)
 
+            self.QR = [qsets[l].QR[b:b + 1].contiguous() for l in range(L)]
+
         def layer(self, l):
-            msa.route_scores(queries[l].QR, store.KRbar[l], d, out=self.S)
+            a = att_q[l][self.b]
+            msa.route_scores(self.QR[l], store.KRbar[l], d, out=self.S)
             msa.select_topk(self.S, dco, d, doc_scores=self.ds, ws=self.ws_sel, outs=self.outs)
-            msa.sparse_attend(atts[l].Q, atts[l].K_loc, atts[l].V_loc, store.Kbar, store.Vbar, dco,
+            msa.sparse_attend(a.Q, a.K_loc, a.V_loc, store.Kbar, store.Vbar, dco,
                               self.outs[0][0], self.outs[2], max_sel, d=d, ws=self.ws_att,
                               out=self.out)
 
@@ -904,22 +918,24 @@ def pipeline_on(args, store, queries, atts, Qn):
                 ctypes.byref(d), Qn, N)), dtype=torch.uint8, device=dev)
             need = msa.lib().msa_route_scores_workspace(ctypes.byref(d), Qn, 1, C)
             self.ws_route = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
-            self.ws_att = torch.empty(msa.sparse_attend_workspace(
-                1, atts[0].K_loc.shape[0], max_sel, d), dtype=torch.uint8, device=dev)
-            self.out = [torch.empty((1, 32, 128), dtype=torch.bfloat16, device=dev)
-                        for _ in range(Qn)]
-            # each query's router rows of every layer (the layer inputs are shared)
-            self.QR = [queries[l].QR.expand(Qn, -1, -1, -1).contiguous() for l in range(L)]
+            self.ws_att = torch.empty(msa.lib().msa_sparse_attend_batch_workspace(
+                ctypes.byref(d), Qn, 1, atts[0].K_loc.shape[0], max_sel), dtype=torch.uint8,
+                device=dev)
+            self.out = torch.empty((Qn, 1, 32, 128), dtype=torch.bfloat16, device=dev)
+            # every query's router rows, query rows and local context, per layer
+            self.QR = [qsets[l].QR for l in range(L)]
+            self.Q = [torch.stack([a.Q for a in att_q[l]]) for l in range(L)]
+            self.K = [torch.stack([a.K_loc for a in att_q[l]]) for l in range(L)]
+            self.V = [torch.stack([a.V_loc for a in att_q[l]]) for l in range(L)]
 
         def layer(self, l):
             msa.route_scores(self.QR[l], store.KRbar[l], d, out=self.S, ws=self.ws_route)
             msa.select_topk(self.S, dco, d, doc_scores=self.ds, ws=self.ws_sel, outs=self.outs)
-            for b in range(Qn):
-                msa.sparse_attend(atts[l].Q, atts[l].K_loc, atts[l].V_loc, store.Kbar, store.Vbar,
-                                  dco, self.outs[0][b], self.outs[2][b:b + 1], max_sel, d=d,
-                                  ws=self.ws_att, out=self.out[b])
+            msa.sparse_attend_batch(self.Q[l], self.K[l], self.V[l], store.Kbar, store.Vbar, dco,
+                                    self.outs[0], self.outs[2], max_sel, d=d, ws=self.ws_att,
+                                    out=self.out)
 
-    lanes = [Lane() for _ in range(Qn)]
+    lanes = [Lane(b) for b in range(Qn)]
     batch = Batch()
     torch.cuda.synchronize()
 
@@ -972,20 +988,20 @@ def pipeline_on(args, store, queries, atts, Qn):
             with torch.cuda.stream(ln.stream):
                 ln.layer(l)
             ln.stream.synchronize()
-            assert set(queries[l].planted_docs[0]) <= set(ln.outs[0][0].cpu().tolist())
+            assert set(qsets[l].planted_docs[ln.b]) <= set(ln.outs[0][0].cpu().tolist())
     for l in range(L):
         batch.layer(l)
         torch.cuda.synchronize()
         ids = batch.outs[0].cpu()
         for b in range(Qn):
-            assert set(queries[l].planted_docs[0]) <= set(ids[b].tolist())
+            assert set(qsets[l].planted_docs[b]) <= set(ids[b].tolist())
     ms_c, ms_s, ms_b = float(np.mean(conc)), float(np.mean(seq)), float(np.mean(bat))
     tokens = C * TOKENS_PER_CHUNK
     # the value is the faster of the two concurrent schedules
     batched = ms_b < ms_c
     ms_v = ms_b if batched else ms_c
-    schedule = ("batched: per layer one routing scan and selection for all queries, then each "
-                "query's attention" if batched else "one stream per query")
+    schedule = ("batched: per layer one routing scan, one selection and one attention call for "
+                "all queries" if batched else "one stream per query")
     r = base_result(args, "memory tokens routed/sec (all concurrent queries)",
                     Qn * L * tokens / (ms_v * 1e-3), "tokens/s", ms_v,
                     {"workload": f"{Qn} concurrent decode queries, {L} routed layers each, over a "

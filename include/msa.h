@@ -104,7 +104,7 @@ const char* msa_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
 int32_t msa_abi_version(void);
-#define MSA_ABI_VERSION 5
+#define MSA_ABI_VERSION 6
 
 /* ------------------------------------------------------------------------ */
 /* Chunk plan (host, pure). Each document is cut into ceil(n_i / chunk)
@@ -254,6 +254,36 @@ int32_t msa_sparse_attend(const msa_dims* d, const msa_bf16* Q, int32_t M, const
                           const int32_t* sel_ids, const int32_t* n_sel, int64_t max_sel_chunks,
                           int64_t pos0, msa_bf16* out, float* out_f32, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* msa_sparse_attend for B queries of one shape in one set of launches (the
+ * same stage, techblg section M routing bullet: each query attends over its
+ * own selection and its own local context), e.g. concurrent decode queries
+ * routed together by one msa_route_topk call. Each query computes exactly
+ * what msa_sparse_attend computes for it alone (bit for bit).
+ *   Q [B, M, n_q_heads, 128], K_loc and V_loc [B, M_loc, n_kv_heads, 128]
+ *     bf16, packed (query b at b * M and b * M_loc rows); k_loc_rotated as
+ *     in msa_sparse_attend, for every query.
+ *   Kbar, Vbar, kv_on_host, n_chunks, doc_chunk_offsets, n_docs: the shared
+ *     pooled store, as in msa_sparse_attend.
+ *   sel_ids [B, top_k] int32 and n_sel [B] int32 (device): each query's
+ *     selection, e.g. the topk_ids and n_sel of msa_route_topk.
+ *   pos0: as in msa_sparse_attend, the same for every query (-1 means each
+ *     query's own n_sel).
+ *   out [B, M, n_q_heads, 128] bf16 (written); out_f32 optional, same shape.
+ *   ws / ws_bytes: at least msa_sparse_attend_batch_workspace() bytes.
+ *   B >= 1; B times the call's key splits must stay within 65,535
+ *   (MSA_ERR_SHAPE otherwise; at most 255 queries always fit). Errors as in
+ *   msa_sparse_attend. */
+size_t msa_sparse_attend_batch_workspace(const msa_dims* d, int32_t B, int32_t M, int32_t M_loc,
+                                         int64_t max_sel_chunks);
+int32_t msa_sparse_attend_batch(const msa_dims* d, const msa_bf16* Q, int32_t B, int32_t M,
+                                const msa_bf16* K_loc, const msa_bf16* V_loc, int32_t M_loc,
+                                int32_t k_loc_rotated, const msa_bf16* Kbar, const msa_bf16* Vbar,
+                                int32_t kv_on_host, int64_t n_chunks,
+                                const int64_t* doc_chunk_offsets, int32_t n_docs,
+                                const int32_t* sel_ids, const int32_t* n_sel,
+                                int64_t max_sel_chunks, int64_t pos0, msa_bf16* out,
+                                float* out_f32, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Memory Interleave (techblg section M, Memory Interleave bullet; chooseai.io

@@ -13,5 +13,5 @@ from ._lib import (  # noqa: F401
     DOC_ROPE_CHUNK, DOC_ROPE_TOKEN, EXPORTED, LIB_PATH, NOALLOC_SCRATCH_BYTES, STORE_K, STORE_KR, STORE_V,
     TOKEN_REDUCE_MAX, TOKEN_REDUCE_MEAN, Dims, Interleave, InterleaveBatch, MsaError, Store, dims, encode_pool,
     lib, plan_chunks, route_aux_loss, route_topk, route_topk_noalloc, route_scores, route_topk_workspace, select_topk, sparse_attend,
-    sparse_attend_workspace, store_file_info,
+    sparse_attend_batch, sparse_attend_workspace, store_file_info,
 )

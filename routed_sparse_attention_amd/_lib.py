@@ -32,6 +32,7 @@ EXPORTED = [
     "msa_store_save", "msa_store_load", "msa_store_file_info", "msa_route_aux_loss_workspace",
     "msa_route_aux_loss", "msa_route_topk_noalloc", "msa_interleave_batch_reset",
     "msa_interleave_batch_step_workspace", "msa_interleave_batch_step",
+    "msa_sparse_attend_batch_workspace", "msa_sparse_attend_batch",
 ]
 NOALLOC_SCRATCH_BYTES = 16 << 20   # MSA_NOALLOC_SCRATCH_BYTES
 STORE_KR, STORE_K, STORE_V = 1, 2, 4   # tensor bits of a store file
@@ -107,6 +108,10 @@ def lib() -> ctypes.CDLL:
         "msa_sparse_attend_workspace": (_sz, [_DP, _i32, _i32, _i64]),
         "msa_sparse_attend": (_i32, [_DP, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i64,
                                      _vp, _i32, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
+        "msa_sparse_attend_batch_workspace": (_sz, [_DP, _i32, _i32, _i32, _i64]),
+        "msa_sparse_attend_batch": (_i32, [_DP, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _vp,
+                                           _i32, _i64, _vp, _i32, _vp, _vp, _i64, _i64, _vp, _vp,
+                                           _vp, _sz, _vp]),
         "msa_interleave_reset": (_i32, [ctypes.POINTER(InterleaveStateC), _i32, _vp]),
         "msa_interleave_step_workspace": (_sz, [_DP, _i32, _i32, _i64, _i32, _i64]),
         "msa_interleave_step": (_i32, [_DP, ctypes.POINTER(InterleaveStateC), _vp, _vp, _vp, _vp,
@@ -352,6 +357,46 @@ def sparse_attend(Q, K_loc, V_loc, Kbar, Vbar, doc_chunk_offsets, sel_ids, n_sel
                                    doc_chunk_offsets.numel() - 1, _p(sel_ids), _p(n_sel),
                                    max_sel_chunks, pos0, _p(out), _p(of), _p(ws), ws.numel(),
                                    _stream()))
+    return (out, of) if want_f32 else out
+
+
+def sparse_attend_batch(Q, K_loc, V_loc, Kbar, Vbar, doc_chunk_offsets, sel_ids, n_sel,
+                        max_sel_chunks: int, pos0: int = -1, k_loc_rotated: bool = False,
+                        d: Dims | None = None, want_f32: bool = False, ws=None, out=None):
+    """Stage-3 sparse attention for B queries of one shape in one set of
+    launches: Q [B, M, Hq, 128], K_loc / V_loc [B, M_loc, 8, 128], sel_ids
+    [B, top_k], n_sel [B]; returns out bf16 [B, M, Hq, 128] (and fp32 when
+    want_f32). Each query's result equals sparse_attend's for it alone."""
+    d = d or dims()
+    _need(Q, "Q", torch.bfloat16, ndim=4)
+    _need(K_loc, "K_loc", torch.bfloat16, ndim=4)
+    _need(V_loc, "V_loc", torch.bfloat16, ndim=4)
+    on_host = Kbar.device.type == "cpu"
+    for t, n in ((Kbar, "Kbar"), (Vbar, "Vbar")):
+        _need(t, n, torch.bfloat16, device_kind=None, ndim=3)
+        if (t.device.type == "cpu") != on_host:
+            raise ValueError("Kbar and Vbar must both be on the GPU or both in pinned host memory")
+        if on_host and not t.is_pinned():
+            raise ValueError(f"{n}: host memory must be pinned")
+    _need(doc_chunk_offsets, "doc_chunk_offsets", torch.int64)
+    _need(sel_ids, "sel_ids", torch.int32, ndim=2)
+    _need(n_sel, "n_sel", torch.int32)
+    B, M, M_loc = Q.shape[0], Q.shape[1], K_loc.shape[1]
+    if K_loc.shape[0] != B or V_loc.shape[:2] != K_loc.shape[:2] or sel_ids.shape[0] != B \
+            or n_sel.numel() != B:
+        raise ValueError("sparse_attend_batch: every input needs the same batch size B")
+    dev = Q.device
+    if out is None:
+        out = torch.empty(Q.shape, dtype=torch.bfloat16, device=dev)
+    of = torch.empty(Q.shape, dtype=torch.float32, device=dev) if want_f32 else None
+    need = lib().msa_sparse_attend_batch_workspace(ctypes.byref(d), B, M, M_loc, max_sel_chunks)
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, dev)
+    _check(lib().msa_sparse_attend_batch(
+        ctypes.byref(d), _p(Q), B, M, _p(K_loc), _p(V_loc), M_loc, int(bool(k_loc_rotated)),
+        _p(Kbar), _p(Vbar), int(on_host), Kbar.shape[0], _p(doc_chunk_offsets),
+        doc_chunk_offsets.numel() - 1, _p(sel_ids), _p(n_sel), max_sel_chunks, pos0, _p(out),
+        _p(of), _p(ws), ws.numel(), _stream()))
     return (out, of) if want_f32 else out
 
 

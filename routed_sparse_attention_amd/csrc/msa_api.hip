@@ -456,6 +456,52 @@ int32_t msa_sparse_attend(const msa_dims* d, const msa_bf16* Q, int32_t M, const
   return launch_attend(a, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
+size_t msa_sparse_attend_batch_workspace(const msa_dims* d, int32_t B, int32_t M, int32_t M_loc,
+                                         int64_t max_sel_chunks) {
+  if (!d || B < 1 || M < 1 || M_loc < M || max_sel_chunks < 0) return 0;
+  return attend_workspace(M, M_loc, d->n_q_heads, max_sel_chunks, B);
+}
+
+int32_t msa_sparse_attend_batch(const msa_dims* d, const msa_bf16* Q, int32_t B, int32_t M,
+                                const msa_bf16* K_loc, const msa_bf16* V_loc, int32_t M_loc,
+                                int32_t k_loc_rotated, const msa_bf16* Kbar, const msa_bf16* Vbar,
+                                int32_t kv_on_host, int64_t n_chunks, const int64_t* dco,
+                                int32_t n_docs, const int32_t* sel_ids, const int32_t* n_sel,
+                                int64_t max_sel_chunks, int64_t pos0, msa_bf16* out,
+                                float* out_f32, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (B < 1) return fail(MSA_ERR_SHAPE, "attend_batch: B=%d must be >= 1", B);
+  rc = check_attend_args(d, Q, M, K_loc, V_loc, M_loc, Kbar, Vbar, n_chunks, dco, n_docs, sel_ids,
+                         n_sel, max_sel_chunks, out);
+  if (rc) return rc;
+  const size_t need = attend_workspace(M, M_loc, d->n_q_heads, max_sel_chunks, B);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "attend_batch workspace: need %zu bytes, got %zu", need,
+                ws_bytes);
+  const void* kb = nullptr;
+  const void* vb = nullptr;
+  rc = resolve_kv(Kbar, kv_on_host, &kb, "Kbar");
+  if (rc) return rc;
+  rc = resolve_kv(Vbar, kv_on_host, &vb, "Vbar");
+  if (rc) return rc;
+  AttendArgs a;
+  a.Q = Q; a.M = M; a.n_q_heads = d->n_q_heads;
+  a.K_loc = K_loc; a.V_loc = V_loc; a.M_loc = M_loc; a.k_loc_rotated = k_loc_rotated;
+  a.Kbar = static_cast<const uint16_t*>(kb); a.Vbar = static_cast<const uint16_t*>(vb);
+  a.n_chunks = n_chunks; a.dco = dco; a.n_docs = n_docs;
+  a.sel_ids = sel_ids; a.n_sel = n_sel; a.top_k = d->top_k;
+  a.max_sel_chunks = max_sel_chunks; a.pos0 = pos0; a.theta = (double)d->rope_theta;
+  a.kv_on_host = kv_on_host ? 1 : 0;
+  a.out = out; a.out_f32 = out_f32;
+  AttendBatch ab;
+  ab.nb = B;
+  ab.q_stride = (int64_t)M * d->n_q_heads * kDim;
+  ab.kv_stride = (int64_t)M_loc * kRowElems;
+  return launch_attend(a, ws, ws_bytes, static_cast<hipStream_t>(stream), B > 1 ? &ab : nullptr);
+}
+
 int32_t msa_interleave_reset(msa_interleave_state* st, int32_t n_docs, void* stream) {
   clear_error();
   if (!st || !st->doc_scores) return fail(MSA_ERR_INVALID_ARG, "interleave_reset: NULL state");
@@ -549,13 +595,9 @@ int32_t msa_interleave_batch_reset(msa_interleave_batch* st, int32_t n_docs, voi
 
 namespace {
 // Queries of a batched interleave round attended per set of launches: up to
-// kAttendGroup when the multi-token kernel serves the shape (their partials
-// share the workspace), else one.
+// kAttendGroup (their partials share the workspace).
 constexpr int32_t kAttendGroup = 8;
-int32_t attend_group(int32_t B, int32_t M_new, int32_t n_q_heads) {
-  if (!attend_is_multi(M_new, n_q_heads)) return 1;
-  return B < kAttendGroup ? B : kAttendGroup;
-}
+int32_t attend_group(int32_t B) { return B < kAttendGroup ? B : kAttendGroup; }
 }  // namespace
 
 extern "C" {
@@ -568,7 +610,7 @@ size_t msa_interleave_batch_step_workspace(const msa_dims* d, int32_t B, int32_t
     return 0;
   const size_t r = route_topk_ws(B, M_new, n_chunks, n_docs, d->top_k);
   const size_t a = attend_workspace(M_new, cap_loc, d->n_q_heads, max_sel_chunks,
-                                    attend_group(B, M_new, d->n_q_heads));
+                                    attend_group(B));
   return r > a ? r : a;
 }
 
@@ -602,7 +644,7 @@ int32_t msa_interleave_batch_step(const msa_dims* d, msa_interleave_batch* st,
   rc = check_attend_args(d, Q_new, M_new, st->K_loc, st->V_loc, M_loc, Kbar, Vbar, n_chunks, dco,
                          n_docs, st->topk_ids, st->n_sel, max_sel_chunks, out);
   if (rc) return rc;
-  const int32_t grp = attend_group(B, M_new, d->n_q_heads);
+  const int32_t grp = attend_group(B);
   const size_t need_r = route_topk_ws(B, M_new, n_chunks, n_docs, d->top_k);
   const size_t need_a = attend_workspace(M_new, M_loc, d->n_q_heads, max_sel_chunks, grp);
   if (ws == nullptr || ws_bytes < need_r || ws_bytes < need_a)

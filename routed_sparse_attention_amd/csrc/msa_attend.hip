@@ -12,10 +12,8 @@
 // and local keys causal; logits scale 1/sqrt(128); q head h reads KV head
 // h / (Hq / 8); memory chunks enter in rank order.
 //
-// Pipeline (one stream, two launches; three when several row blocks share
-// the local keys):
-//   rot_k     (only then) rotates K_loc into the workspace, one thread per
-//             rotation pair, so that each local key is rotated once;
+// Pipeline (one stream, two launches) for up to 32 query rows per KV head
+// (decode; several queries of a batch share the launches):
 //   attn      flash attention, one wave per (32 query rows of one KV group,
 //             KV head, key split), about 2048 waves. Each wave first builds
 //             the chunk list of the selected documents itself (their ranges
@@ -93,30 +91,17 @@ struct AttnArgs {
   int64_t max_sel; int64_t pos0;
   float qk_scale_log2;
   float* Opart; float* ML;
+  // queries of a batch: blockIdx.z = query · n_splits + split; per-query
+  // element strides of Q, the local keys and values, the partials and the
+  // (m, l) pairs (selection: top_k ids and one n_sel per query)
+  int32_t n_splits;
+  int64_t q_stride, kl_stride, op_stride, ml_stride;
   RopeTab rt;
 };
 
 __device__ __forceinline__ int clamp_nsel(const int32_t* n_sel, int top_k) {
   int ns = *n_sel;
   return ns < 0 ? 0 : (ns > top_k ? top_k : ns);
-}
-
-// Local keys rotated once into the workspace: K rows v·8 + g at pos0 + v.
-__global__ __launch_bounds__(256) void rot_k_kernel(const uint16_t* __restrict__ Kl, int32_t M_loc,
-                                                    const int32_t* __restrict__ n_sel,
-                                                    int32_t top_k, int64_t pos0_arg, RopeTab rt,
-                                                    uint16_t* __restrict__ Kr) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)M_loc * kHeads * (kDim / 2)) return;
-  const int64_t pos0 = pos0_arg < 0 ? (int64_t)clamp_nsel(n_sel, top_k) : pos0_arg;
-  const int64_t row = idx / (kDim / 2);
-  const int m = (int)(idx % (kDim / 2));
-  double sn, cs;
-  sincos((double)(pos0 + row / kHeads) * rt.om[m], &sn, &cs);
-  const uint16_t* src = Kl + row * kDim;
-  const double x = bf16f(src[m]), y = bf16f(src[m + 64]);
-  Kr[row * kDim + m] = d2bf(x * cs - y * sn);
-  Kr[row * kDim + m + 64] = d2bf(y * cs + x * sn);
 }
 
 // The attention workgroup is one wave: LDS traffic between its lanes is
@@ -206,21 +191,28 @@ void attn_kernel(const AttnArgs a) {
   const int half = lane >> 5;     // which 8-wide k slice this lane holds
   const int rb = blockIdx.x;      // row block within the KV group
   const int g = blockIdx.y;       // KV head
-  const int split = blockIdx.z;
+  const int qb = blockIdx.z / a.n_splits;          // query of the batch
+  const int split = blockIdx.z - qb * a.n_splits;
   const int G = a.Hq / kHeads;    // query heads per KV head
   const int rows_g = a.M * G;
   const int64_t n_rows_tot = (int64_t)a.M * a.Hq;
+  // this query's rows, local context, selection and partials (uniform)
+  const uint16_t* Qq = a.Q + qb * a.q_stride;
+  const int32_t* sel_ids = a.sel_ids + (int64_t)qb * a.top_k;
+  const int32_t* n_sel = a.n_sel + qb;
+  float* Opart = a.Opart + qb * a.op_stride;
+  float* MLq = a.ML + qb * a.ml_stride;
   gbf16* Kbar = uniform_ptr(a.Kbar);
   gbf16* Vbar = uniform_ptr(a.Vbar);
-  gbf16* Kloc = uniform_ptr(a.Kloc);
-  gbf16* Vloc = uniform_ptr(a.Vloc);
+  gbf16* Kloc = uniform_ptr(a.Kloc + qb * a.kl_stride);
+  gbf16* Vloc = uniform_ptr(a.Vloc + qb * a.kl_stride);
 
   // the query rows are loaded first: their loads overlap the chunk-list ones
   uint4 qa[8];
   const int r = rb * kRowTile + col;
   if (r < rows_g) {
     const int u = r / G, h = g * G + r % G;
-    const uint4* qrow = reinterpret_cast<const uint4*>(a.Q + ((int64_t)u * a.Hq + h) * kDim);
+    const uint4* qrow = reinterpret_cast<const uint4*>(Qq + ((int64_t)u * a.Hq + h) * kDim);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qa[ks] = qrow[ks * 2 + half];
   } else {
@@ -234,8 +226,8 @@ void attn_kernel(const AttnArgs a) {
   // ---- chunk ranges of the selected documents, in rank order: lane i holds
   //      document i's range; a key's place in the memory part is the prefix
   //      sum of the ranges before it, cut at max_sel
-  const int32_t id = lane < a.top_k ? a.sel_ids[lane] : -1;   // loaded with n_sel
-  const int ns = clamp_nsel(a.n_sel, a.top_k);
+  const int32_t id = lane < a.top_k ? sel_ids[lane] : -1;   // loaded with n_sel
+  const int ns = clamp_nsel(n_sel, a.top_k);
   int64_t start = 0, cnt = 0;
   if (lane < ns) {
     if (id >= 0 && id < a.n_docs) {
@@ -259,7 +251,7 @@ void attn_kernel(const AttnArgs a) {
     s_start[lane] = start;
   }
   const int n_keys = n_mem + a.M_loc;
-  const int key_split = split_keys(n_keys, (int)gridDim.z, kKeyTile);
+  const int key_split = split_keys(n_keys, a.n_splits, kKeyTile);
   const int k_begin = split * key_split;
   const int k_end = min(k_begin + key_split, n_keys);
   const int64_t pos0 = a.pos0 < 0 ? (int64_t)ns : a.pos0;
@@ -492,10 +484,10 @@ void attn_kernel(const AttnArgs a) {
     const int u = r / G, h = g * G + r % G;
     const int64_t grow = (int64_t)split * n_rows_tot + (int64_t)u * a.Hq + h;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) a.Opart[grow * kDim + db * 32 + col] = O[db][v];
+    for (int db = 0; db < 4; ++db) Opart[grow * kDim + db * 32 + col] = O[db][v];
     if (col == 0) {
-      a.ML[grow * 2] = mrow[v];
-      a.ML[grow * 2 + 1] = lpart[v];
+      MLq[grow * 2] = mrow[v];
+      MLq[grow * 2 + 1] = lpart[v];
     }
   }
 }
@@ -505,13 +497,21 @@ void attn_kernel(const AttnArgs a) {
 // zero partial, so its weight exp2(-inf - max) = 0 drops it); the sum runs
 // in split order.
 constexpr int kCombineBatch = 64;
-__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ Opart,
-                                                      const float* __restrict__ ML,
+__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ Opart_all,
+                                                      const float* __restrict__ ML_all,
                                                       int32_t n_splits, int64_t n_rows,
+                                                      int64_t op_stride, int64_t ml_stride,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ out_f32) {
+  // one workgroup per output row of a batch of queries (n_rows each); query
+  // qb's partials at qb·op_stride / qb·ml_stride, its rows after the
+  // previous queries'
   __shared__ float ms[kMaxSplits], ls[kMaxSplits];
-  const int64_t row = blockIdx.x;
+  const int64_t row_all = blockIdx.x;
+  const int64_t qb = row_all / n_rows;
+  const int64_t row = row_all - qb * n_rows;
+  const float* Opart = Opart_all + qb * op_stride;
+  const float* ML = ML_all + qb * ml_stride;
   const int d = threadIdx.x;
   float x[kCombineBatch];
 #pragma unroll
@@ -541,8 +541,8 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
     }
   }
   const float o = L > 0.0f ? acc / L : 0.0f;
-  out[row * kDim + d] = f2bf(o);
-  if (out_f32) out_f32[row * kDim + d] = o;
+  out[row_all * kDim + d] = f2bf(o);
+  if (out_f32) out_f32[row_all * kDim + d] = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -996,7 +996,6 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t* __res
 struct AttnPlan {
   bool multi;                 // the multi-token kernel (more than 32 rows per KV head)
   int32_t row_blocks, key_split, n_splits;
-  bool rot_inline;
   size_t off_kr, off_qr, off_opart, off_ml, total;
   int64_t kr_q, qr_q, op_q, ml_q;   // per-query elements of each workspace part
 };
@@ -1011,10 +1010,9 @@ AttnPlan attn_plan(int32_t M, int32_t M_loc, int32_t Hq, int64_t max_sel, int32_
   p.multi = rows_g > kRowTile;
   const int32_t block_rows = p.multi ? kMtRows : kRowTile;
   const int32_t tile_keys = p.multi ? kMtKeys : kKeyTile;
+  // (the one-wave kernel serves up to 32 rows per KV head: one row block,
+  // so each local key is read, and rotated, by one wave per KV head)
   p.row_blocks = (rows_g + block_rows - 1) / block_rows;
-  // with one row block every local key is read by one wave per KV head, so
-  // it is rotated where it is read; otherwise once, by a rotation kernel
-  p.rot_inline = !p.multi && p.row_blocks == 1;
   const int64_t max_keys = max_sel + M_loc;
   // one-wave kernel: aim for >= 2048 waves (8 per CU: one tile's loads of
   // each in flight while the others compute); multi-token kernel: about one
@@ -1067,17 +1065,17 @@ size_t attend_workspace(int32_t M, int32_t M_loc, int32_t n_q_heads, int64_t max
   return attn_plan(M, M_loc, n_q_heads, max_sel_chunks, nb).total;
 }
 
-bool attend_is_multi(int32_t M, int32_t n_q_heads) {
-  return M * (n_q_heads / kHeads) > kRowTile;
-}
 
 int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
                   const AttendBatch* batch) {
   const int32_t nb = batch ? batch->nb : 1;
   const AttnPlan p = attn_plan(a.M, a.M_loc, a.n_q_heads, a.max_sel_chunks, nb);
   if (ws_bytes < p.total) return fail(MSA_ERR_WORKSPACE, "attend workspace too small");
-  if (nb > 1 && (!p.multi || batch->q_stride != (int64_t)a.M * a.n_q_heads * kDim))
-    return fail(MSA_ERR_UNSUPPORTED, "batched attention: multi-token shapes with packed queries only");
+  if (nb > 1 && batch->q_stride != (int64_t)a.M * a.n_q_heads * kDim)
+    return fail(MSA_ERR_UNSUPPORTED, "batched attention: packed queries only");
+  if ((int64_t)p.n_splits * nb > 65535)
+    return fail(MSA_ERR_SHAPE, "batched attention: %d queries x %d key splits exceed the grid",
+                nb, p.n_splits);
   char* base = static_cast<char*>(ws);
   uint16_t* Kr = reinterpret_cast<uint16_t*>(base + p.off_kr);
   float* Opart = reinterpret_cast<float*>(base + p.off_opart);
@@ -1127,7 +1125,7 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
     AttnArgs k;
     k.Q = a.Q; k.M = a.M; k.Hq = a.n_q_heads;
     k.Kloc = a.K_loc; k.Vloc = a.V_loc; k.M_loc = a.M_loc;
-    k.rot_inline = (!a.k_loc_rotated && p.rot_inline) ? 1 : 0;
+    k.rot_inline = a.k_loc_rotated ? 0 : 1;
     k.Kbar = a.Kbar; k.Vbar = a.Vbar; k.n_chunks = a.n_chunks;
     k.dco = a.dco; k.n_docs = a.n_docs;
     k.sel_ids = a.sel_ids; k.n_sel = a.n_sel; k.top_k = a.top_k;
@@ -1135,24 +1133,23 @@ int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
     k.qk_scale_log2 = qk_scale_log2;
     k.Opart = Opart;
     k.ML = ML;
+    k.n_splits = p.n_splits;
+    k.q_stride = batch ? batch->q_stride : 0;
+    k.kl_stride = batch ? batch->kv_stride : 0;
+    k.op_stride = p.op_q;
+    k.ml_stride = p.ml_q;
     k.rt = rt;
-    if (!a.k_loc_rotated && !p.rot_inline) {
-      const int64_t pairs = (int64_t)a.M_loc * kHeads * (kDim / 2);
-      hipLaunchKernelGGL(rot_k_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s,
-                         a.K_loc, a.M_loc, a.n_sel, a.top_k, a.pos0, k.rt, Kr);
-      MSA_LAUNCH_CHECK("rot_k_kernel launch");
-      k.Kloc = Kr;
-    }
+    const dim3 grid(p.row_blocks, kHeads, p.n_splits * nb);
     if (a.kv_on_host)
-      hipLaunchKernelGGL(attn_kernel<true>, dim3(p.row_blocks, kHeads, p.n_splits), dim3(64), 0, s, k);
+      hipLaunchKernelGGL(attn_kernel<true>, grid, dim3(64), 0, s, k);
     else
-      hipLaunchKernelGGL(attn_kernel<false>, dim3(p.row_blocks, kHeads, p.n_splits), dim3(64), 0, s, k);
+      hipLaunchKernelGGL(attn_kernel<false>, grid, dim3(64), 0, s, k);
     MSA_LAUNCH_CHECK("attn_kernel launch");
   }
 
   const int64_t n_rows = (int64_t)a.M * a.n_q_heads;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)n_rows), dim3(kDim), 0, s, Opart, ML,
-                     p.n_splits, n_rows, a.out, a.out_f32);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(n_rows * nb)), dim3(kDim), 0, s, Opart, ML,
+                     p.n_splits, n_rows, p.op_q, p.ml_q, a.out, a.out_f32);
   MSA_LAUNCH_CHECK("combine_kernel launch");
   return MSA_OK;
 }

@@ -303,8 +303,9 @@ struct AttendArgs {
   int32_t kv_on_host;             // K̄/V̄ are pinned host memory (read over PCIe)
   uint16_t* out; float* out_f32;
 };
-// Several queries of one shape in one set of launches (multi-token kernel
-// only): query b's Q and output at b·q_stride elements from a.Q / a.out, its
+// Several queries of one shape in one set of launches: query b's Q and
+// output at b·q_stride elements from a.Q / a.out (packed: q_stride is
+// M · n_q_heads · 128), its
 // local K/V at b·kv_stride from a.K_loc / a.V_loc, its selection at
 // a.sel_ids + b·top_k and a.n_sel + b. Each query computes exactly what it
 // would alone.
@@ -314,7 +315,6 @@ struct AttendBatch {
 };
 size_t attend_workspace(int32_t M, int32_t M_loc, int32_t n_q_heads, int64_t max_sel_chunks,
                         int32_t nb = 1);
-bool attend_is_multi(int32_t M, int32_t n_q_heads);
 int launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
                   const AttendBatch* batch = nullptr);
 

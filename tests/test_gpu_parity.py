@@ -356,6 +356,55 @@ def test_attend_decode():
     _attend_case(1, 129, counts, list(range(3, 19)), 72)
 
 
+@pytest.mark.parametrize("M,M_loc,B,host_kv,k_rot", [(1, 129, 5, True, False), (1, 40, 3, False, True),
+                                                     (8, 40, 2, False, False), (64, 96, 3, False, False)])
+def test_attend_batch_equals_single_queries(M, M_loc, B, host_kv, k_rot):
+    """msa_sparse_attend_batch: B queries of one shape, each with its own
+    query rows, local context and selection (some invalid ids, one query
+    with fewer documents), attend in one set of launches; each query's
+    output equals, bit for bit, what msa_sparse_attend gives it alone, and
+    one query is checked against the oracle. Decode shapes (the one-wave
+    kernel, K̄/V̄ in HBM or pinned host memory, local keys rotated by the
+    caller or not) and a multi-token shape."""
+    _banner(f"attend batch B={B} M={M} M_loc={M_loc} host_kv={host_kv} k_rot={k_rot}")
+    rng = synth.np_rng(90 + M, B)
+    counts = rng.integers(1, 40, size=60)
+    st = synth.pooled_store(counts, 90 + M, "cpu", with_kv=True)
+    dco_h = st.doc_chunk_offsets
+    d = msa.dims()
+    atts = [synth.attend_inputs(M, M_loc, 91 + b) for b in range(B)]
+    sels = [[int(x) for x in rng.choice(60, size=16 if b != 1 else 9, replace=False)]
+            for b in range(B)]
+    ids = np.full((B, 16), -1, np.int32)
+    for b in range(B):
+        ids[b, :len(sels[b])] = sels[b]
+    ids[0, 3] = 1000                      # an invalid id is skipped
+    ns = np.array([len(x) for x in sels], np.int32)
+    if host_kv:
+        Kb, Vb = st.Kbar.pin_memory(), st.Vbar.pin_memory()
+    else:
+        Kb, Vb = st.Kbar.to(DEV), st.Vbar.to(DEV)
+    dco = torch.from_numpy(dco_h).to(DEV)
+    max_sel = 16 * int(np.diff(dco_h).max())
+    Q = torch.stack([a.Q for a in atts]).to(DEV)
+    K = torch.stack([a.K_loc for a in atts]).to(DEV)
+    V = torch.stack([a.V_loc for a in atts]).to(DEV)
+    ids_t, ns_t = torch.from_numpy(ids).to(DEV), torch.from_numpy(ns).to(DEV)
+    out = msa.sparse_attend_batch(Q, K, V, Kb, Vb, dco, ids_t, ns_t, max_sel, k_loc_rotated=k_rot,
+                                  d=d)
+    singles = [msa.sparse_attend(Q[b], K[b], V[b], Kb, Vb, dco, ids_t[b], ns_t[b:b + 1], max_sel,
+                                 k_loc_rotated=k_rot, d=d) for b in range(B)]
+    torch.cuda.synchronize()
+    for b in range(B):
+        assert torch.equal(out[b].view(torch.int16), singles[b].view(torch.int16)), b
+    # the oracle over query 0's valid ids in order, at the GPU's pos0 = n_sel
+    # (which counts the invalid id)
+    sel0 = [int(x) for x in ids[0] if 0 <= x < 60]
+    ref = O.sparse_attend(u16(atts[0].Q), u16(atts[0].K_loc), u16(atts[0].V_loc), u16(st.Kbar),
+                          u16(st.Vbar), dco_h, sel0, int(ns[0]), k_rot)
+    assert_attn_close(O.bf16_to_f64(u16(out[0])), ref, "batched query 0")
+
+
 def test_attend_decode_host_kv():
     _banner("attend decode pinned host KV")
     counts = [33, 64, 5, 12, 64, 64, 1, 9, 40, 2, 64, 30, 18, 7, 64, 50, 11]

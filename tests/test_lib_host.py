@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = msa.lib()
     for name in _declared():
         assert hasattr(L, name), f"libmsa.so does not export {name}"
-    assert L.msa_abi_version() == 5
+    assert L.msa_abi_version() == 6
 
 
 def test_default_dims_follow_the_pages():
