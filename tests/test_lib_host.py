@@ -162,6 +162,29 @@ def test_store_validation_before_any_gpu_work():
     assert rc == -1 and b"staging" in L.msa_last_error()
 
 
+def test_attend_batch_validation_and_workspace():
+    """msa_sparse_attend_batch checks its arguments on the host like
+    msa_sparse_attend (an empty batch, a context shorter than the query, too
+    small a workspace) and touches no device memory; its workspace grows with
+    the batch, one query's equal to msa_sparse_attend's."""
+    L = msa.lib()
+    d = msa.dims()
+    p = ctypes.c_void_p(16)
+    args = lambda B, M, M_loc, ws_bytes: (ctypes.byref(d), p, B, M, p, p, M_loc, 0, p, p, 0, 8, p, 2,
+                                          p, p, 8, -1, p, None, p, ws_bytes, None)
+    assert L.msa_sparse_attend_batch(*args(0, 1, 4, 1 << 30)) == -2
+    assert b"B=0" in L.msa_last_error()
+    assert L.msa_sparse_attend_batch(*args(2, 5, 4, 1 << 30)) == -2
+    assert b"M_loc" in L.msa_last_error()
+    assert L.msa_sparse_attend_batch(*args(2, 1, 4, 16)) == -3
+    one = msa.sparse_attend_workspace(1, 129, 1024, d)
+    w = [L.msa_sparse_attend_batch_workspace(ctypes.byref(d), B, 1, 129, 1024) for B in (1, 2, 8)]
+    assert w[0] == one and w[0] < w[1] < w[2]
+    assert L.msa_sparse_attend_batch_workspace(ctypes.byref(d), 0, 1, 129, 1024) == 0
+    assert L.msa_sparse_attend_batch_workspace(ctypes.byref(d), 4, 64, 768, 2048) > \
+        msa.sparse_attend_workspace(64, 768, 2048, d)
+
+
 def test_attend_workspace_covers_every_smaller_context():
     """A workspace sized for cap_loc local tokens serves every smaller context
     (interleave rounds reuse one): the size is monotone in M_loc."""
