@@ -948,10 +948,14 @@ void attn_mt_kernel(const MtArgs args) {
 }
 
 // Merges the key splits of the multi-token kernel: 32 threads per output
-// row, 4 dims each (8-byte loads of the bf16 partials O_s / l_s); every
-// split's (m, l) is read first, then the partials are weighted by
-// exp2(m_s - max) · l_s and summed in split order.
+// row, 4 dims each (8-byte loads of the bf16 partials O_s / l_s); the
+// partials are weighted by exp2(m_s - max) · l_s and summed in split order.
+// The (m, l) pairs and partials of the first kCombRegs splits are loaded
+// together, before the maximum is known, so the merge waits for one memory
+// round trip instead of two; later splits (more than the multi-token plan
+// makes at its usual shapes) are read in a second loop.
 constexpr int kCombRows = 8;
+constexpr int kCombRegs = 8;
 __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t* __restrict__ Opart_all,
                                                            const float* __restrict__ ML_all,
                                                            int32_t n_splits, int64_t n_rows,
@@ -970,20 +974,38 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t* __res
   uint16_t* out = out_all + qb * n_rows * kDim;
   float* out_f32 = out_f32_all ? out_f32_all + qb * n_rows * kDim : nullptr;
   const int d = (threadIdx.x & 31) * 4;
+  float2 ml[kCombRegs];
+  uint2 xs[kCombRegs];
+#pragma unroll
+  for (int s = 0; s < kCombRegs; ++s) {
+    if (s < n_splits) {
+      const int64_t gr = (int64_t)s * n_rows + row;
+      ml[s] = *reinterpret_cast<const float2*>(ML + gr * 2);
+      xs[s] = *reinterpret_cast<const uint2*>(Opart + gr * kDim + d);
+    }
+  }
   float mx = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, ML[((int64_t)s * n_rows + row) * 2]);
+#pragma unroll
+  for (int s = 0; s < kCombRegs; ++s)
+    if (s < n_splits) mx = fmaxf(mx, ml[s].x);
+  for (int s = kCombRegs; s < n_splits; ++s) mx = fmaxf(mx, ML[((int64_t)s * n_rows + row) * 2]);
   float L = 0.0f;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  auto add = [&](float m, float l, uint2 x) {
+    const float w = exp2f(m - mx) * l;
+    L += w;
+    acc.x += w * bf16lo(x.x);
+    acc.y += w * bf16hi(x.x);
+    acc.z += w * bf16lo(x.y);
+    acc.w += w * bf16hi(x.y);
+  };
   if (mx != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
+#pragma unroll
+    for (int s = 0; s < kCombRegs; ++s)
+      if (s < n_splits) add(ml[s].x, ml[s].y, xs[s]);
+    for (int s = kCombRegs; s < n_splits; ++s) {
       const int64_t gr = (int64_t)s * n_rows + row;
-      const float w = exp2f(ML[gr * 2] - mx) * ML[gr * 2 + 1];
-      L += w;
-      const uint2 x = *reinterpret_cast<const uint2*>(Opart + gr * kDim + d);
-      acc.x += w * bf16lo(x.x);
-      acc.y += w * bf16hi(x.x);
-      acc.z += w * bf16lo(x.y);
-      acc.w += w * bf16hi(x.y);
+      add(ML[gr * 2], ML[gr * 2 + 1], *reinterpret_cast<const uint2*>(Opart + gr * kDim + d));
     }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
