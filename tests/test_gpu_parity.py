@@ -428,6 +428,16 @@ def test_attend_long_local():
     _attend_case(256, 700, counts, [10, 11, 0, 5, 12, 3], 76)
 
 
+def test_attend_many_splits():
+    """33 query tokens are 132 rows per KV head: two row blocks, so the
+    multi-token plan aims at 16 key splits; 896 selected chunks + 40 local
+    keys (capacity 939 keys, 15 tiles of 64) give 15 splits, more than the
+    merge holds in registers, so its second loop over the splits runs."""
+    _banner("attend M=33 M_loc=40, 15 key splits")
+    counts = [64] * 14 + [5, 9]
+    _attend_case(33, 40, counts, list(range(14)), 80)
+
+
 @pytest.mark.parametrize("M,M_loc,pos0", [(1, 40, 70_000), (3, 35, 1_000_003), (8, 71, 12_345),
                                            (9, 40, 123_456), (1, 33, -1)])
 def test_attend_rope_positions(M, M_loc, pos0):
