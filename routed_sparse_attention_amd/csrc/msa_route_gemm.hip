@@ -591,7 +591,9 @@ int launch_scan_gemm(const uint16_t* QR, int32_t B, int32_t M, const uint16_t* K
   g.n_row_tiles = (int32_t)(g.n_rows / rows);
   g.parts = scan_gemm_parts(M);
   const int64_t qthreads = g.n_rows * kHeads;
-  hipLaunchKernelGGL(qhat_rows_kernel, dim3((unsigned)((qthreads + 255) / 256)), dim3(256), 0, s,
+  // one-wave workgroups: a 256-token query's 2,048 (row, head) threads spread
+  // over 32 CUs instead of 8 (each thread's loads are 16 strided 16-byte reads)
+  hipLaunchKernelGGL(qhat_rows_kernel, dim3((unsigned)((qthreads + 63) / 64)), dim3(64), 0, s,
                      QR, g.n_rows, qhat);
   MSA_LAUNCH_CHECK("qhat_rows_kernel launch");
   // 256-chunk tiles when they give at least two workgroups per CU, else 128
